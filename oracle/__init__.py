@@ -1,0 +1,18 @@
+"""fp64 CPU oracle of MoBA causal prefill (test infrastructure only).
+
+Only the tests, the package smoke check and the benchmark's CPU-baseline leg use
+this package. It shares no code with the HIP library and imports nothing from it.
+"""
+from .moba_oracle import (  # noqa: F401
+    attended_count,
+    attended_keys,
+    attended_pairs_closed_form,
+    gate_scores,
+    moba_ref,
+    n_blocks,
+    pooled_keys,
+    pooled_keys_fp32,
+    select_blocks,
+    select_row,
+    sparsity,
+)

@@ -1,0 +1,244 @@
+"""Plain fp64 CPU oracle of the MoBA causal prefill forward pass.
+
+TEST INFRASTRUCTURE ONLY. This module is imported by the test-suite, by the
+package smoke check and by the benchmark's CPU-baseline leg; the product path
+never imports, calls or executes anything here. It shares no code, header,
+table or helper with the HIP library.
+
+What it computes (one sequence, H heads, head size D, block size B, n = N/B):
+
+1. Block partition: the context of N tokens is cut into n blocks of B
+   contiguous tokens (Moonshot MoBA report as summarised by 智东西,
+   section 二 "block partition", B = N/n).
+2. Mean-pooled block key K̄_i = mean of the B keys of block i ("score_pooling:
+   mean" in the configuration snippet, section 3 of the wzjinhao.cn MoBA
+   engineering article; pomoai MoBA overview, "核心原理" step 2).
+3. Parameter-less gate: score g_i = <q_t, K̄_i>, no scale, no learned weights
+   (same sources; 智东西 section 二, relevance score s_i).
+4. Causal top-k: block j = floor(t/B) is always chosen and causally masked;
+   among past blocks i < j the k-1 best scores are added; no future block is
+   ever chosen (wzjinhao.cn article section 3, the causal_mask and
+   current_block_force switches; 智东西 section 二, causality paragraph;
+   aliyun article, "MoBA 的技术原理" causality item). The list is returned in
+   ascending block order (the block-select snippet of wzjinhao.cn section 4
+   sorts its result).
+5. Attention over the chosen keys: softmax(q·kᵀ/√D)·v restricted to the
+   attended set A(t) (0539edu.com NSA/MoBA explainer, section 1 formula).
+   The per-block partial outputs merged by log-sum-exp that the pages describe
+   (pomoai overview step 3; 智东西 section 二 steps 3-5) are only a faster route
+   to this one softmax, so the oracle evaluates the softmax directly.
+
+Readings of points the pages leave open (each one is listed in the design notes):
+
+* top_k counts the forced current block (k blocks in total; the configuration
+  section of the wzjinhao.cn article says a token sees exactly k blocks and
+  derives sparsity 1 - B*k/N from it).
+* When fewer than k blocks are eligible (j < k-1) every block 0..j is chosen
+  and the selection row is padded with -1.
+* Exact score ties are broken toward the lower block index.
+* The gate decision is taken in fp32, the precision of the pages' block-select
+  snippet (float32 keys and query): K̄ is the exact mean rounded once to fp32,
+  and each score is the exact dot product of q with that fp32 K̄, rounded once
+  to fp32. Everything else (the attention, the log-sum-exp) is fp64.
+* The softmax scale is 1/√D; lse is the natural log of the sum of
+  exp(q·k/√D) over A(t).
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def n_blocks(N: int, block_size: int) -> int:
+    """Number of blocks n = N / B; the partition needs B to divide N."""
+    if block_size < 1 or N < 1 or N % block_size != 0:
+        raise ValueError(f"block_size {block_size} must divide N {N}")
+    return N // block_size
+
+
+def pooled_keys(k: np.ndarray, block_size: int) -> np.ndarray:
+    """Exact (fp64) mean of the keys of every block: [H, n, D].
+
+    ``k`` is [N, H, D]; its values are widened exactly to fp64.
+    """
+    N, H, D = k.shape
+    n = n_blocks(N, block_size)
+    k64 = np.asarray(k, dtype=np.float64).reshape(n, block_size, H, D)
+    total = np.zeros((n, H, D), dtype=np.float64)
+    for r in range(block_size):          # fixed order, one key of every block at a time
+        total += k64[:, r]
+    return np.ascontiguousarray((total / block_size).transpose(1, 0, 2))
+
+
+def pooled_keys_fp32(k: np.ndarray, block_size: int) -> np.ndarray:
+    """The block mean keys rounded once to fp32 (the gate's precision): [H, n, D]."""
+    return pooled_keys(k, block_size).astype(np.float32)
+
+
+def gate_scores(q_rows: np.ndarray, kbar32_h: np.ndarray) -> np.ndarray:
+    """fp32 gate scores of query rows against every block of one head.
+
+    ``q_rows`` [R, D] (one head), ``kbar32_h`` [n, D] fp32 mean keys. The dot
+    products are formed in fp64 (exact to fp64 rounding for bf16/fp32 inputs)
+    and rounded once to fp32. Returns [R, n] float32; future blocks are not
+    masked here.
+    """
+    s = np.asarray(q_rows, np.float64) @ np.asarray(kbar32_h, np.float64).T
+    return s.astype(np.float32)
+
+
+def select_row(scores_row: np.ndarray, j: int, topk: int) -> list[int]:
+    """Causal top-k for one query in block j from its fp32 block scores.
+
+    Returns the chosen blocks in ascending order: block j plus the k-1 highest
+    scoring past blocks, ranked by score (descending) then block index
+    (ascending); all of 0..j when j+1 <= k.
+    """
+    if j + 1 <= topk:
+        return list(range(j + 1))
+    past = [(-float(scores_row[i]), i) for i in range(j)]
+    past.sort()
+    chosen = [i for _, i in past[:topk - 1]]
+    return sorted(chosen + [j])
+
+
+def select_blocks(q: np.ndarray, k: np.ndarray, block_size: int, topk: int,
+                  rows: np.ndarray | None = None, chunk: int = 65536):
+    """Selection of every (head, row): int32 [H, R, topk], ascending, -1 padded.
+
+    ``rows`` defaults to all N query rows. Also returns the fp32 mean keys.
+    """
+    N, H, D = q.shape
+    n = n_blocks(N, block_size)
+    if topk < 1:
+        raise ValueError("topk must be >= 1")
+    kbar32 = pooled_keys_fp32(k, block_size)
+    rows = np.arange(N, dtype=np.int64) if rows is None else np.asarray(rows, np.int64)
+    R = rows.shape[0]
+    sel = np.full((H, R, topk), -1, dtype=np.int32)
+    for h in range(H):
+        for c0 in range(0, R, chunk):
+            rr = rows[c0:c0 + chunk]
+            sc = gate_scores(q[rr, h, :], kbar32[h])          # [r, n]
+            jj = rr // block_size
+            neg = -sc.astype(np.float64)
+            neg[np.arange(n)[None, :] >= jj[:, None]] = np.inf   # only past blocks compete
+            order = np.argsort(neg, axis=1, kind="stable")       # ties keep lower index first
+            for i, (t, j) in enumerate(zip(rr, jj)):
+                if j + 1 <= topk:
+                    row = list(range(j + 1))
+                else:
+                    row = sorted(order[i, :topk - 1].tolist() + [int(j)])
+                sel[h, c0 + i, :len(row)] = row
+    return sel, kbar32
+
+
+def attended_keys(sel_row, t: int, block_size: int) -> np.ndarray:
+    """Key positions A(t): every chosen past block in full, the own block up to t."""
+    j = t // block_size
+    parts = []
+    for b in sel_row:
+        b = int(b)
+        if b < 0:
+            continue
+        if b < j:
+            parts.append(np.arange(b * block_size, (b + 1) * block_size))
+        elif b == j:
+            parts.append(np.arange(j * block_size, t + 1))
+        else:
+            raise ValueError(f"future block {b} chosen for row {t}")
+    return np.concatenate(parts)
+
+
+def _softmax_rows(logits: np.ndarray):
+    m = np.max(logits, axis=-1, keepdims=True)
+    p = np.exp(logits - m)
+    l = np.sum(p, axis=-1, keepdims=True)
+    return p / l, (m + np.log(l))[..., 0]
+
+
+def moba_ref(q, k, v, block_size: int, topk: int, sel=None, rows=None, max_rows_chunk: int = 512):
+    """fp64 MoBA causal prefill.
+
+    Arguments are [N, H, D] arrays (float32 holding exact bf16 or fp32 values).
+    ``sel`` optionally overrides the gate ([H, R, topk] int32 for the same rows).
+    ``rows`` selects query rows to evaluate (default: all, in the dense masked
+    form per query block; otherwise row by row).
+
+    Returns ``(out, lse, sel)``: out [R, H, D] fp64, lse [H, R] fp64 (natural
+    log), sel [H, R, topk] int32.
+    """
+    q = np.asarray(q)
+    N, H, D = q.shape
+    n = n_blocks(N, block_size)
+    if sel is None:
+        sel, _ = select_blocks(q, k, block_size, topk, rows=rows)
+    scale = 1.0 / math.sqrt(D)
+    if rows is not None:
+        rows = np.asarray(rows, np.int64)
+        R = rows.shape[0]
+        out = np.zeros((R, H, D), np.float64)
+        lse = np.zeros((H, R), np.float64)
+        for h in range(H):
+            kh = np.asarray(k[:, h, :], np.float64)
+            vh = np.asarray(v[:, h, :], np.float64)
+            for i, t in enumerate(rows):
+                keys = attended_keys(sel[h, i], int(t), block_size)
+                logits = (kh[keys] @ np.asarray(q[t, h], np.float64)) * scale
+                p, l = _softmax_rows(logits[None, :])
+                out[i, h] = p[0] @ vh[keys]
+                lse[h, i] = l[0]
+        return out, lse, sel
+
+    out = np.zeros((N, H, D), np.float64)
+    lse = np.zeros((H, N), np.float64)
+    B = block_size
+    for h in range(H):
+        qh = np.asarray(q[:, h, :], np.float64)
+        kh = np.asarray(k[:, h, :], np.float64)
+        vh = np.asarray(v[:, h, :], np.float64)
+        for j in range(n):
+            nk = (j + 1) * B
+            key_block = np.arange(nk) // B
+            key_pos = np.arange(nk)
+            for r0 in range(j * B, (j + 1) * B, max_rows_chunk):
+                r1 = min(r0 + max_rows_chunk, (j + 1) * B)
+                t = np.arange(r0, r1)
+                chosen = np.zeros((r1 - r0, n), dtype=bool)
+                for i in range(r1 - r0):
+                    s = sel[h, r0 + i]
+                    chosen[i, s[s >= 0]] = True
+                mask = chosen[:, key_block] & (key_pos[None, :] <= t[:, None])
+                logits = (qh[r0:r1] @ kh[:nk].T) * scale
+                logits = np.where(mask, logits, -np.inf)
+                p, l = _softmax_rows(logits)
+                out[r0:r1, h] = p @ vh[:nk]
+                lse[h, r0:r1] = l
+    return out, lse, sel
+
+
+def attended_count(t: int, block_size: int, topk: int) -> int:
+    """|A(t)| for a row whose selection has min(k, j+1) blocks: c(t)."""
+    j = t // block_size
+    return min(topk - 1, j) * block_size + (t % block_size) + 1
+
+
+def attended_pairs_closed_form(N: int, block_size: int, topk: int) -> int:
+    """Σ_t |A(t)| for one head, in closed form.
+
+    Rows in blocks j < k-1 see all j past blocks, later rows see k-1 of them;
+    each row also sees its own block up to itself.
+    """
+    n = n_blocks(N, block_size)
+    B, k = block_size, topk
+    m = min(k - 1, n)                     # blocks j = 0..m-1 see j past blocks
+    past = B * B * (m * (m - 1) // 2) + B * B * max(n - m, 0) * (k - 1)
+    own = n * B * (B + 1) // 2
+    return past + own
+
+
+def sparsity(N: int, block_size: int, topk: int) -> float:
+    """Fraction of the context a late query does not attend: 1 - B*k/N."""
+    return 1.0 - block_size * min(topk, n_blocks(N, block_size)) / N

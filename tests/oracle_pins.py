@@ -1,0 +1,337 @@
+"""Pins that tie the fp64 oracle to facts fixed outside of it.
+
+Every ``pin_*`` function takes an oracle module ``m`` (the real one, or a copy
+with a planted mistake) and raises ``AssertionError`` when ``m`` disagrees with
+what the pages or the mathematics fix:
+
+* numbers the pages print (tests/golden/pages_pins.json),
+* brute force on tiny inputs through independent routes (exhaustive subset
+  search for the top-k, torch's masked SDPA for the attention),
+* special cases that reduce to a library routine (top_k >= n is full causal
+  attention; top_k = 1 is block-diagonal causal attention),
+* closed forms and invariants.
+"""
+
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_pins.json")
+
+
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _rand(N, H, D, seed, scale=1.0):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((N, H, D)).astype(np.float32) * np.float32(scale)
+    k = rng.standard_normal((N, H, D)).astype(np.float32) * np.float32(scale)
+    v = rng.standard_normal((N, H, D)).astype(np.float32)
+    return q, k, v
+
+
+def _t64(x):
+    return torch.from_numpy(np.asarray(x, np.float64))
+
+
+# ---------------------------------------------------------------------------
+# independent brute force
+# ---------------------------------------------------------------------------
+
+def brute_selection(q, k, B, topk):
+    """Top-k by exhaustive subset search, computed with torch (not numpy).
+
+    For each query the chosen past blocks are the (k-1)-subset of eligible
+    blocks with the largest score sum; among equal sums the lexicographically
+    smallest index tuple wins (that is the lower-index tie rule). The gate
+    scores are the exact dot products with the fp32-rounded block means,
+    rounded to fp32.
+    """
+    N, H, D = q.shape
+    n = N // B
+    kt = _t64(k).reshape(n, B, H, D)
+    kbar = kt.mean(dim=1).to(torch.float32).to(torch.float64)     # [n, H, D]
+    sel = np.full((H, N, topk), -1, np.int64)
+    for h in range(H):
+        sc = (_t64(q[:, h, :]) @ kbar[:, h, :].T).to(torch.float32).to(torch.float64).numpy()
+        for t in range(N):
+            j = t // B
+            if j + 1 <= topk:
+                chosen = list(range(j + 1))
+            else:
+                best, best_sum = None, -math.inf
+                for comb in itertools.combinations(range(j), topk - 1):
+                    s = sum(sc[t, i] for i in comb)
+                    if s > best_sum:
+                        best, best_sum = comb, s
+                chosen = sorted(list(best) + [j])
+            sel[h, t, :len(chosen)] = chosen
+    return sel
+
+
+def brute_attention(q, k, v, B, sel):
+    """Masked attention through torch SDPA in fp64, mask built token by token."""
+    N, H, D = q.shape
+    out = np.zeros((N, H, D))
+    lse = np.zeros((H, N))
+    for h in range(H):
+        mask = torch.zeros((N, N), dtype=torch.bool)
+        for t in range(N):
+            for s in range(t + 1):
+                if (s // B) in set(int(x) for x in sel[h, t] if x >= 0):
+                    mask[t, s] = True
+        qh, kh, vh = _t64(q[:, h]), _t64(k[:, h]), _t64(v[:, h])
+        o = torch.nn.functional.scaled_dot_product_attention(
+            qh[None], kh[None], vh[None], attn_mask=mask[None])
+        out[:, h] = o[0].numpy()
+        logits = (qh @ kh.T) / math.sqrt(D)
+        lse[h] = torch.logsumexp(logits.masked_fill(~mask, -math.inf), dim=-1).numpy()
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# pins
+# ---------------------------------------------------------------------------
+
+TINY_CASES = [  # (N, H, D, B, topk, seed)
+    (16, 2, 4, 2, 3, 11),
+    (32, 1, 4, 4, 2, 12),
+    (48, 2, 4, 4, 4, 13),
+    (64, 1, 4, 8, 3, 14),
+    (40, 1, 4, 8, 1, 15),
+    (24, 2, 4, 2, 5, 16),
+]
+
+
+def pin_bruteforce_tiny(m):
+    for N, H, D, B, topk, seed in TINY_CASES:
+        q, k, v = _rand(N, H, D, seed)
+        out, lse, sel = m.moba_ref(q, k, v, B, topk)
+        bsel = brute_selection(q, k, B, topk)
+        assert np.array_equal(sel, bsel), f"selection differs from exhaustive search at {N, B, topk}"
+        bout, blse = brute_attention(q, k, v, B, bsel)
+        assert np.allclose(out, bout, rtol=0, atol=1e-12), f"output differs from masked SDPA at {N, B, topk}"
+        assert np.allclose(lse, blse, rtol=0, atol=1e-12), f"lse differs from masked logsumexp at {N, B, topk}"
+
+
+def pin_full_causal(m):
+    """top_k >= n selects every past block: plain causal attention."""
+    for N, H, D, B, seed in [(64, 2, 8, 8, 21), (96, 1, 16, 16, 22)]:
+        q, k, v = _rand(N, H, D, seed)
+        n = N // B
+        for topk in (n, n + 3):
+            out, lse, sel = m.moba_ref(q, k, v, B, topk)
+            for h in range(H):
+                qh, kh, vh = _t64(q[:, h]), _t64(k[:, h]), _t64(v[:, h])
+                ref = torch.nn.functional.scaled_dot_product_attention(qh[None], kh[None], vh[None], is_causal=True)[0]
+                assert np.allclose(out[:, h], ref.numpy(), atol=1e-12, rtol=0)
+                logits = (qh @ kh.T) / math.sqrt(D)
+                causal = torch.ones(N, N, dtype=torch.bool).tril()
+                rl = torch.logsumexp(logits.masked_fill(~causal, -math.inf), -1)
+                assert np.allclose(lse[h], rl.numpy(), atol=1e-12, rtol=0)
+
+
+def pin_block_diagonal(m):
+    """top_k = 1 keeps only the own block: block-diagonal causal attention."""
+    N, H, D, B = 64, 2, 8, 16
+    q, k, v = _rand(N, H, D, 31)
+    out, lse, sel = m.moba_ref(q, k, v, B, 1)
+    for h in range(H):
+        for j in range(N // B):
+            s = slice(j * B, (j + 1) * B)
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                _t64(q[s, h])[None], _t64(k[s, h])[None], _t64(v[s, h])[None], is_causal=True)[0]
+            assert np.allclose(out[s, h], ref.numpy(), atol=1e-12, rtol=0)
+    assert np.all(sel[:, :, 0] == (np.arange(N) // B)[None, :])
+
+
+def pin_first_token(m):
+    N, H, D, B = 32, 2, 8, 8
+    q, k, v = _rand(N, H, D, 41)
+    out, lse, _ = m.moba_ref(q, k, v, B, 3)
+    for h in range(H):
+        assert np.array_equal(out[0, h], v[0, h].astype(np.float64))
+        exact = float(np.dot(q[0, h].astype(np.float64), k[0, h].astype(np.float64))) / math.sqrt(D)
+        assert abs(lse[h, 0] - exact) < 1e-13
+
+
+def pin_constant_v(m):
+    N, H, D, B = 48, 1, 8, 8
+    q, k, _ = _rand(N, H, D, 51)
+    v = np.broadcast_to(np.linspace(-2, 2, D, dtype=np.float32), (N, H, D)).copy()
+    out, _, _ = m.moba_ref(q, k, v, B, 3)
+    assert np.allclose(out, v.astype(np.float64), atol=1e-13, rtol=0)
+
+
+def pin_zero_query(m):
+    """q = 0: every score ties, the tie rule alone decides, attention is uniform."""
+    N, H, D, B, topk = 64, 1, 8, 8, 3
+    _, k, v = _rand(N, H, D, 61)
+    q = np.zeros((N, H, D), np.float32)
+    out, lse, sel = m.moba_ref(q, k, v, B, topk)
+    for t in range(N):
+        j = t // B
+        expect = list(range(j + 1)) if j + 1 <= topk else list(range(topk - 1)) + [j]
+        assert list(sel[0, t, :len(expect)]) == expect, (t, sel[0, t])
+        keys = [s for s in range(t + 1) if (s // B) in expect]
+        assert np.allclose(out[t, 0], v[keys, 0].astype(np.float64).mean(0), atol=1e-13)
+        assert abs(lse[0, t] - math.log(len(keys))) < 1e-13
+
+
+def pin_invariants(m):
+    N, H, D, B = 256, 3, 16, 16
+    q, k, v = _rand(N, H, D, 71)
+    for topk in (1, 2, 3, 5, 16, 20):
+        sel, _ = m.select_blocks(q, k, B, topk)
+        for h in range(H):
+            for t in range(N):
+                j = t // B
+                row = [int(x) for x in sel[h, t] if x >= 0]
+                assert len(row) == min(topk, j + 1)
+                assert row == sorted(set(row))
+                assert j in row and max(row) == j and min(row) >= 0
+                assert all(x == -1 for x in sel[h, t, len(row):])
+
+
+def pin_pages_worked_example(m):
+    g = golden()["worked_example"]
+    N, B, topk, D = g["N"], g["block_size"], g["top_k"], g["head_dim"]
+    rng = np.random.default_rng(81)
+    k = rng.standard_normal((N, 1, D)).astype(np.float32)
+    q = rng.standard_normal((N, 1, D)).astype(np.float32)
+    rows = np.array([N - 1])
+    sel, _ = m.select_blocks(q, k, B, topk, rows=rows)
+    chosen = [int(x) for x in sel[0, 0] if x >= 0]
+    assert len(chosen) == g["blocks_selected"]
+    tokens = len(m.attended_keys(sel[0, 0], N - 1, B))
+    assert tokens == g["tokens_attended"]
+    assert round(100 * (1 - tokens / N), 2) == g["sparsity_percent_2dp"]
+    assert round(100 * m.sparsity(N, B, topk), 2) == g["sparsity_percent_2dp"]
+
+
+def pin_pages_sparsity_table(m):
+    rows = golden()["sparsity_table"]["rows"]
+    snippet = golden()["config_snippet"]
+    assert m.n_blocks(snippet["context_length"], snippet["block_size"]) == snippet["num_blocks"]
+    assert round(100 * m.sparsity(snippet["context_length"], snippet["block_size"], snippet["top_k"]), 1) \
+        == snippet["sparsity_percent_1dp"]
+    for r in rows:
+        N, B, topk = r["N"], r["block_size"], r["top_k"]
+        assert round(100 * m.sparsity(N, B, topk), 1) == r["sparsity_percent_1dp"]
+        D = 4
+        rng = np.random.default_rng(91)
+        k = rng.standard_normal((N, 1, D)).astype(np.float32)
+        q = rng.standard_normal((N, 1, D)).astype(np.float32)
+        last = np.array([N - 1])
+        sel, _ = m.select_blocks(q, k, B, topk, rows=last)
+        tokens = len(m.attended_keys(sel[0, 0], N - 1, B))
+        assert round(100 * (1 - tokens / N), 1) == r["sparsity_percent_1dp"]
+
+
+def pin_granularity(m):
+    for c in golden()["granularity"]["cases"]:
+        n, chosen = c["n_blocks"], c["chosen"]
+        B, D = 4, 4
+        N = n * B
+        q, k, _ = _rand(N, 1, D, 101)
+        sel, _ = m.select_blocks(q, k, B, chosen, rows=np.array([N - 1]))
+        tokens = len(m.attended_keys(sel[0, 0], N - 1, B))
+        assert 100 * (1 - tokens / N) == c["sparsity_percent"]
+    f = golden()["full_switch"]
+    assert m.n_blocks(f["N"], f["block_size"]) == f["n_blocks"]
+    assert 100 * m.sparsity(f["N"], f["block_size"], f["top_k"]) == f["sparsity_percent"]
+
+
+def pin_closed_form_pairs(m):
+    for N, B, topk in [(128, 8, 3), (128, 16, 1), (96, 8, 12), (160, 32, 2), (64, 8, 9)]:
+        q, k, _ = _rand(N, 1, 4, 111)
+        sel, _ = m.select_blocks(q, k, B, topk)
+        total = sum(len(m.attended_keys(sel[0, t], t, B)) for t in range(N))
+        # closed form, written independently: sum over query blocks j of
+        # B*B*min(k-1, j) + B*(B+1)/2
+        n = N // B
+        direct = sum(B * B * min(topk - 1, j) + B * (B + 1) // 2 for j in range(n))
+        assert total == direct == m.attended_pairs_closed_form(N, B, topk)
+        assert all(len(m.attended_keys(sel[0, t], t, B)) == m.attended_count(t, B, topk) for t in range(N))
+
+
+def pin_lse_merge(m):
+    """Merging per-block softmax partials by log-sum-exp equals the oracle's one softmax."""
+    N, H, D, B, topk = 96, 2, 8, 8, 4
+    q, k, v = _rand(N, H, D, 121)
+    out, lse, sel = m.moba_ref(q, k, v, B, topk)
+    for h in range(H):
+        for t in range(N):
+            j = t // B
+            parts = []
+            for b in sel[h, t]:
+                if b < 0:
+                    continue
+                hi = (b + 1) * B if b < j else t + 1
+                ks = torch.from_numpy(k[b * B:hi, h].astype(np.float64))
+                vs = torch.from_numpy(v[b * B:hi, h].astype(np.float64))
+                lg = ks @ torch.from_numpy(q[t, h].astype(np.float64)) / math.sqrt(D)
+                parts.append((torch.logsumexp(lg, 0), torch.softmax(lg, 0) @ vs))
+            tot = torch.logsumexp(torch.stack([p[0] for p in parts]), 0)
+            merged = sum(torch.exp(p[0] - tot) * p[1] for p in parts)
+            assert abs(float(tot) - lse[h, t]) < 1e-12
+            assert np.allclose(merged.numpy(), out[t, h], atol=1e-12, rtol=0)
+
+
+def pin_pooling_linearity(m):
+    """Dot with the mean key equals the mean of the per-key dot products."""
+    N, H, D, B = 64, 2, 8, 16
+    q, k, _ = _rand(N, H, D, 131)
+    kbar = m.pooled_keys(k, B)
+    assert kbar.shape == (H, N // B, D)
+    for h in range(H):
+        for t in range(0, N, 7):
+            for i in range(N // B):
+                per_key = [float(np.dot(q[t, h].astype(np.float64), k[s, h].astype(np.float64)))
+                           for s in range(i * B, (i + 1) * B)]
+                assert abs(math.fsum(per_key) / B - float(q[t, h].astype(np.float64) @ kbar[h, i])) < 1e-12
+
+
+def pin_gate_rounding(m):
+    """Mean keys and scores are the exact values rounded once to fp32."""
+    from fractions import Fraction
+    N, H, D, B = 32, 1, 4, 8
+    q, k, _ = _rand(N, H, D, 141)
+    kb32 = m.pooled_keys_fp32(k, B)
+    for i in range(N // B):
+        for d in range(D):
+            exact = sum(Fraction(float(k[s, 0, d])) for s in range(i * B, (i + 1) * B)) / B
+            assert kb32[0, i, d] == np.float32(float(exact))
+    sc = m.gate_scores(q[:, 0, :], kb32[0])
+    for t in range(N):
+        for i in range(N // B):
+            exact = sum(Fraction(float(q[t, 0, d])) * Fraction(float(kb32[0, i, d])) for d in range(D))
+            assert sc[t, i] == np.float32(float(exact))
+
+
+def pin_row_mode_matches(m):
+    """Row-by-row evaluation equals the dense masked evaluation."""
+    N, H, D, B, topk = 128, 2, 8, 16, 3
+    q, k, v = _rand(N, H, D, 151)
+    out, lse, sel = m.moba_ref(q, k, v, B, topk)
+    rows = np.array([0, 5, 16, 17, 63, 100, 127])
+    o2, l2, s2 = m.moba_ref(q, k, v, B, topk, rows=rows)
+    assert np.array_equal(s2, sel[:, rows])
+    assert np.allclose(o2, out[rows], atol=1e-13, rtol=0)
+    assert np.allclose(l2, lse[:, rows], atol=1e-13, rtol=0)
+
+
+ALL_PINS = [
+    pin_bruteforce_tiny, pin_full_causal, pin_block_diagonal, pin_first_token, pin_constant_v,
+    pin_zero_query, pin_invariants, pin_pages_worked_example, pin_pages_sparsity_table,
+    pin_granularity, pin_closed_form_pairs, pin_lse_merge, pin_pooling_linearity,
+    pin_gate_rounding, pin_row_mode_matches,
+]

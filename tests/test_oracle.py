@@ -1,0 +1,73 @@
+"""CPU tests: the oracle against its pins, and planted mistakes that the pins catch."""
+
+import importlib.util
+import os
+import sys
+import types
+
+import pytest
+
+import oracle
+import oracle.moba_oracle as om
+from tests import oracle_pins as P
+
+ORACLE_SRC = os.path.join(os.path.dirname(os.path.dirname(__file__)), "oracle", "moba_oracle.py")
+
+
+@pytest.mark.parametrize("pin", P.ALL_PINS, ids=lambda f: f.__name__)
+def test_oracle_pin(pin):
+    pin(om)
+
+
+def test_package_exports():
+    for name in ("moba_ref", "select_blocks", "pooled_keys", "sparsity", "attended_pairs_closed_form"):
+        assert hasattr(oracle, name)
+
+
+# Each mutation plants one plausible mistake in a copy of the oracle's source.
+MUTATIONS = {
+    "no_forced_current_block": ("sorted(order[i, :topk - 1].tolist() + [int(j)])",
+                                "sorted(order[i, :topk].tolist())"),
+    "causal_mask_off_by_one": ("key_pos[None, :] <= t[:, None]", "key_pos[None, :] < t[:, None] + 2"),
+    "future_blocks_compete": ("neg[np.arange(n)[None, :] >= jj[:, None]] = np.inf",
+                              "neg[np.arange(n)[None, :] > jj[:, None]] = np.inf"),
+    "ascending_scores": ("neg = -sc.astype(np.float64)", "neg = sc.astype(np.float64)"),
+    "scale_1_over_d": ("scale = 1.0 / math.sqrt(D)", "scale = 1.0 / D"),
+    "pool_sum_not_mean": ("return np.ascontiguousarray((total / block_size).transpose(1, 0, 2))",
+                          "return np.ascontiguousarray(total.transpose(1, 0, 2))"),
+    "pool_wrong_axis": ("total += k64[:, r]", "total += k64[:, r][:, ::-1]"),
+    "unstable_ties": ('order = np.argsort(neg, axis=1, kind="stable")',
+                      'order = np.argsort(neg[:, ::-1], axis=1, kind="stable"); order = neg.shape[1] - 1 - order'),
+    "lse_base2": ("return p / l, (m + np.log(l))[..., 0]", "return p / l, (m + np.log2(l))[..., 0]"),
+    "own_block_full": ("parts.append(np.arange(j * block_size, t + 1))",
+                       "parts.append(np.arange(j * block_size, (j + 1) * block_size))"),
+    "no_fp32_gate_rounding": ("return s.astype(np.float32)", "return s"),
+    "pool_fp32_not_rounded": ("return pooled_keys(k, block_size).astype(np.float32)",
+                              "return pooled_keys(k, block_size).astype(np.float16).astype(np.float32)"),
+    "pad_with_zero": ("sel = np.full((H, R, topk), -1, dtype=np.int32)",
+                      "sel = np.full((H, R, topk), 0, dtype=np.int32)"),
+    "transposed_scores": ("s = np.asarray(q_rows, np.float64) @ np.asarray(kbar32_h, np.float64).T",
+                          "s = (np.asarray(q_rows, np.float64)[:, ::-1] @ np.asarray(kbar32_h, np.float64).T)"),
+    "softmax_without_max": ("p = np.exp(logits - m)", "p = np.exp(logits - m * 0.5)"),
+}
+
+
+def _mutant(name, old, new):
+    src = open(ORACLE_SRC).read()
+    assert src.count(old) == 1, f"mutation {name} no longer applies"
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    mod.__file__ = ORACLE_SRC
+    exec(compile(src.replace(old, new), f"<mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name):
+    mod = _mutant(name, *MUTATIONS[name])
+    caught = []
+    for pin in P.ALL_PINS:
+        try:
+            pin(mod)
+        except Exception as e:  # AssertionError, or a crash caused by the mistake
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin catches the planted mistake {name}"
