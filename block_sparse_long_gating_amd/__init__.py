@@ -1,0 +1,141 @@
+"""Python binding of libmoba, the MI355X (gfx950) MoBA causal prefill library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C-ABI declared in ``include/moba.h``. PyTorch provides the
+device memory and the current stream. There is no fallback: if ``libmoba.so``
+is missing or a call fails, an exception is raised.
+
+Tensors are row-major ``[N, H, D]`` (token, head, dim) on a CUDA (HIP) device,
+bf16 or fp32; ``lse`` is ``[H, N]`` fp32; ``sel`` is ``[H, N, topk]`` int32.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["prefill", "gate_topk", "block_mean_keys", "MobaError", "library_path", "load_library",
+           "STATUS", "MAX_TOPK", "MAX_BLOCKS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmoba.so")
+_lib = None
+
+STATUS = {0: "MOBA_OK", 1: "MOBA_ERR_INVALID_ARG", 2: "MOBA_ERR_UNSUPPORTED", 3: "MOBA_ERR_HIP",
+          4: "MOBA_ERR_OUT_OF_MEMORY"}
+MAX_TOPK = 32
+MAX_BLOCKS = 4096
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+
+_SIGNATURES = {
+    "moba_block_mean_keys": [_P, _P, _I64, _I32, _I32, _I32, _P],
+    "moba_block_mean_keys_f32": [_P, _P, _I64, _I32, _I32, _I32, _P],
+    "moba_gate_topk": [_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P],
+    "moba_gate_topk_f32": [_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P],
+    "moba_prefill_fwd": [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P],
+    "moba_prefill_fwd_f32": [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P],
+    "moba_status_string": [ctypes.c_int],
+    "moba_last_hip_error": [],
+}
+
+
+class MobaError(RuntimeError):
+    def __init__(self, status: int, where: str, hip_error: int = 0):
+        name = STATUS.get(status, f"status {status}")
+        msg = f"{where}: {name}" + (f" (hipError {hip_error})" if status == 3 else "")
+        super().__init__(msg)
+        self.status = status
+        self.hip_error = hip_error
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libmoba.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        for name, args in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_char_p if name == "moba_status_string" else ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MobaError(status, where, load_library().moba_last_hip_error() if status == 3 else 0)
+
+
+def _stream(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_qkv(*ts):
+    import torch
+    t0 = ts[0]
+    if t0.dim() != 3:
+        raise ValueError("expected [N, H, D] tensors")
+    if t0.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("tensors must be bfloat16 or float32")
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on a GPU device")
+        if t.shape != t0.shape or t.dtype != t0.dtype or t.device != t0.device:
+            raise ValueError("q, k, v must share shape, dtype and device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [N, H, D]")
+    N, H, D = t0.shape
+    return N, H, D, t0.dtype == torch.float32
+
+
+def block_mean_keys(k, block_size: int):
+    """Block mean keys, fp32 ``[H, N // block_size, D]``."""
+    import torch
+    N, H, D, f32 = _check_qkv(k)
+    lib = load_library()
+    n = N // block_size if block_size > 0 else 0
+    kbar = torch.empty((H, max(n, 1), D), dtype=torch.float32, device=k.device)
+    fn = lib.moba_block_mean_keys_f32 if f32 else lib.moba_block_mean_keys
+    _check(fn(k.data_ptr(), kbar.data_ptr(), N, H, D, block_size, _stream(k.device)), "moba_block_mean_keys")
+    return kbar
+
+
+def gate_topk(q, k, block_size: int, topk: int):
+    """Chosen blocks per (head, query): int32 ``[H, N, topk]``, ascending, -1 padded."""
+    import torch
+    N, H, D, f32 = _check_qkv(q, k)
+    lib = load_library()
+    sel = torch.empty((H, N, max(topk, 1)), dtype=torch.int32, device=q.device)
+    fn = lib.moba_gate_topk_f32 if f32 else lib.moba_gate_topk
+    _check(fn(q.data_ptr(), k.data_ptr(), sel.data_ptr(), N, H, D, block_size, topk, _stream(q.device)),
+           "moba_gate_topk")
+    return sel
+
+
+def prefill(q, k, v, block_size: int, topk: int, out=None, lse=None):
+    """MoBA causal prefill. Returns ``(out [N,H,D], lse [H,N] fp32)``."""
+    import torch
+    N, H, D, f32 = _check_qkv(q, k, v)
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, N), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [H, N] tensor")
+    fn = lib.moba_prefill_fwd_f32 if f32 else lib.moba_prefill_fwd
+    _check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), N, H, D, block_size, topk,
+              _stream(q.device)), "moba_prefill_fwd")
+    return out, lse

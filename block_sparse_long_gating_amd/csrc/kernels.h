@@ -1,0 +1,42 @@
+// Launchers of the libmoba kernels (host side). Every launcher only enqueues on
+// `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace moba {
+
+// Parameters of the gate / CSR / attention / merge stages of one call.
+struct Problem {
+  int64_t N;
+  int H, D, B, n, topk;
+  int lmax;        // largest number of past blocks a query keeps: min(topk - 1, n - 1)
+  int ntiles;      // ceil(N / kQTile) gate tiles per head
+  int64_t p_off;   // total number of (query, past block) pairs over all heads
+  int64_t max_items;   // upper bound on off-diagonal work items
+  int64_t diag_items;  // own-block work items: H * n * ceil(B / kQTile)
+  bool is_f32;
+};
+
+hipError_t launch_pool(const void* k, bool is_f32, float* kbar, bf16* pieces, int64_t N, int H, int D, int B,
+                       hipStream_t stream);
+
+// Gate + causal top-k; writes sel and, when `ws_csr` is true, the per-tile
+// counts and in-tile ranks of the off-diagonal selections.
+hipError_t launch_gate(const Problem& p, const void* q, const Workspace& ws, int32_t* sel, bool ws_csr,
+                       hipStream_t stream);
+
+// Scans, list scatter and work-list construction.
+hipError_t launch_csr(const Problem& p, const Workspace& ws, const int32_t* sel, hipStream_t stream);
+
+// Block attention over the off-diagonal work items and the own-block items.
+hipError_t launch_attention(const Problem& p, const void* q, const void* k, const void* v, const Workspace& ws,
+                            int num_cus, hipStream_t stream);
+
+// Log-sum-exp merge of the partial outputs into out and lse.
+hipError_t launch_merge(const Problem& p, const Workspace& ws, void* out, float* lse, hipStream_t stream);
+
+}  // namespace moba

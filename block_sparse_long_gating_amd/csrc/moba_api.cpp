@@ -1,0 +1,300 @@
+// C-ABI of libmoba: argument checks, workspace layout and the launch sequence
+// (pool -> gate/top-k -> query lists -> block attention -> merge). Every entry
+// point only enqueues on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <mutex>
+
+#include "../../include/moba.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceState {
+  std::once_flag once;
+  hipError_t init_error = hipSuccess;
+  bool gfx950 = false;
+  int num_cus = 0;
+  hipMemPool_t pool = nullptr;
+};
+
+DeviceState g_devices[kMaxDevices];
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = static_cast<int>(e);
+  return MOBA_ERR_HIP;
+}
+
+void init_device(int dev, DeviceState* st) {
+  hipDeviceProp_t prop;
+  hipError_t e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) {
+    st->init_error = e;
+    return;
+  }
+  st->gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  st->num_cus = prop.multiProcessorCount;
+  hipMemPoolProps props;
+  std::memset(&props, 0, sizeof(props));
+  props.allocType = hipMemAllocationTypePinned;
+  props.handleTypes = hipMemHandleTypeNone;
+  props.location.type = hipMemLocationTypeDevice;
+  props.location.id = dev;
+  e = hipMemPoolCreate(&st->pool, &props);
+  if (e != hipSuccess) {
+    st->init_error = e;
+    return;
+  }
+  uint64_t keep = ~0ull;  // keep freed workspace in the pool across calls
+  e = hipMemPoolSetAttribute(st->pool, hipMemPoolAttrReleaseThreshold, &keep);
+  if (e != hipSuccess) st->init_error = e;
+}
+
+// Resolves the current device; returns a moba status.
+int current_device(DeviceState** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return MOBA_ERR_UNSUPPORTED;
+  DeviceState* st = &g_devices[dev];
+  std::call_once(st->once, init_device, dev, st);
+  if (st->init_error != hipSuccess) return hip_fail(st->init_error);
+  if (!st->gfx950) return MOBA_ERR_UNSUPPORTED;
+  *out = st;
+  return MOBA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape checks shared by every entry point (no HIP calls).
+int check_shape(int64_t N, int32_t H, int32_t D, int32_t B) {
+  if (N < 1 || H < 1 || B < 1) return MOBA_ERR_INVALID_ARG;
+  if (N % B != 0) return MOBA_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return MOBA_ERR_UNSUPPORTED;
+  if (B % 64 != 0) return MOBA_ERR_UNSUPPORTED;
+  if (N >= (int64_t{1} << 28)) return MOBA_ERR_UNSUPPORTED;
+  if (N / B > MOBA_MAX_BLOCKS) return MOBA_ERR_UNSUPPORTED;
+  if (H > 65535) return MOBA_ERR_UNSUPPORTED;
+  return MOBA_OK;
+}
+
+int check_topk(int64_t N, int32_t B, int32_t topk) {
+  if (topk < 1) return MOBA_ERR_INVALID_ARG;
+  const int64_t n = N / B;
+  if (topk > MOBA_MAX_TOPK && topk < n) return MOBA_ERR_UNSUPPORTED;
+  return MOBA_OK;
+}
+
+moba::Problem make_problem(int64_t N, int32_t H, int32_t D, int32_t B, int32_t topk, bool is_f32) {
+  moba::Problem p;
+  p.N = N;
+  p.H = H;
+  p.D = D;
+  p.B = B;
+  p.n = static_cast<int>(N / B);
+  p.topk = topk;
+  p.lmax = static_cast<int>(std::min<int64_t>(topk - 1, p.n - 1));
+  p.ntiles = static_cast<int>((N + moba::kQTile - 1) / moba::kQTile);
+  int64_t pairs_per_head = 0;  // sum over blocks j of B * min(topk - 1, j)
+  for (int j = 0; j < p.n; ++j) pairs_per_head += static_cast<int64_t>(B) * std::min(topk - 1, j);
+  p.p_off = pairs_per_head * H;
+  p.max_items = p.p_off / moba::kQTile + static_cast<int64_t>(H) * p.n;
+  p.diag_items = static_cast<int64_t>(H) * p.n * ((B + moba::kQTile - 1) / moba::kQTile);
+  p.is_f32 = is_f32;
+  return p;
+}
+
+struct Layout {
+  size_t total = 0;
+  size_t add(size_t bytes) {
+    const size_t o = total;
+    total += (bytes + 255) & ~size_t{255};
+    return o;
+  }
+};
+
+// Workspace offsets for the requested stages.
+struct WsPlan {
+  size_t kbar, kpieces, cnt, totals, offs, rk, qidx, inv, items, counters, part_diag, lse_diag, part_off, lse_off,
+      sel;
+  size_t total;
+};
+
+WsPlan plan(const moba::Problem& p, bool full) {
+  Layout L;
+  WsPlan w;
+  std::memset(&w, 0, sizeof(w));
+  const int64_t hn = static_cast<int64_t>(p.H) * p.n;
+  const int64_t hN = static_cast<int64_t>(p.H) * p.N;
+  const size_t es = p.is_f32 ? 4 : 2;
+  w.kbar = L.add(hn * p.D * 4);
+  w.kpieces = L.add(p.is_f32 ? 0 : hn * 3 * p.D * 2);
+  if (full) {
+    w.cnt = L.add(hn * p.ntiles * 4);
+    w.totals = L.add(hn * 4);
+    w.offs = L.add(hn * 4);
+    w.rk = L.add(hN * p.lmax * 4);
+    w.qidx = L.add(p.p_off * 4);
+    w.inv = L.add(hN * p.lmax * 4);
+    w.items = L.add(p.max_items * sizeof(moba::WorkItem));
+    w.counters = L.add(16 * 4);
+    w.part_diag = L.add(hN * p.D * es);
+    w.lse_diag = L.add(hN * 4);
+    w.part_off = L.add(p.p_off * p.D * es);
+    w.lse_off = L.add(p.p_off * 4);
+    w.sel = L.add(hN * p.topk * 4);
+  }
+  w.total = L.total;
+  return w;
+}
+
+moba::Workspace bind(const WsPlan& w, char* base, bool full) {
+  moba::Workspace ws;
+  std::memset(&ws, 0, sizeof(ws));
+  ws.kbar = reinterpret_cast<float*>(base + w.kbar);
+  ws.kpieces = reinterpret_cast<moba::bf16*>(base + w.kpieces);
+  if (full) {
+    ws.cnt = reinterpret_cast<int32_t*>(base + w.cnt);
+    ws.totals = reinterpret_cast<int32_t*>(base + w.totals);
+    ws.offs = reinterpret_cast<int32_t*>(base + w.offs);
+    ws.rk = reinterpret_cast<int32_t*>(base + w.rk);
+    ws.qidx = reinterpret_cast<int32_t*>(base + w.qidx);
+    ws.inv = reinterpret_cast<int32_t*>(base + w.inv);
+    ws.items = reinterpret_cast<moba::WorkItem*>(base + w.items);
+    ws.counters = reinterpret_cast<int32_t*>(base + w.counters);
+    ws.part_diag = base + w.part_diag;
+    ws.lse_diag = reinterpret_cast<float*>(base + w.lse_diag);
+    ws.part_off = base + w.part_off;
+    ws.lse_off = reinterpret_cast<float*>(base + w.lse_off);
+    ws.sel = reinterpret_cast<int32_t*>(base + w.sel);
+  }
+  return ws;
+}
+
+int alloc_ws(DeviceState* st, size_t bytes, hipStream_t stream, char** out) {
+  void* p = nullptr;
+  hipError_t e = hipMallocFromPoolAsync(&p, bytes ? bytes : 256, st->pool, stream);
+  if (e == hipErrorOutOfMemory) {
+    (void)hipGetLastError();
+    return MOBA_ERR_OUT_OF_MEMORY;
+  }
+  if (e != hipSuccess) return hip_fail(e);
+  *out = static_cast<char*>(p);
+  return MOBA_OK;
+}
+
+int finish(hipError_t launch_error, char* ws, hipStream_t stream) {
+  hipError_t fe = hipFreeAsync(ws, stream);
+  if (launch_error != hipSuccess) return hip_fail(launch_error);
+  if (fe != hipSuccess) return hip_fail(fe);
+  return MOBA_OK;
+}
+
+int block_mean_keys_impl(const void* k, float* kbar, int64_t N, int32_t H, int32_t D, int32_t B, hipStream_t stream,
+                         bool is_f32) {
+  if (k == nullptr || kbar == nullptr) return MOBA_ERR_INVALID_ARG;
+  int s = check_shape(N, H, D, B);
+  if (s != MOBA_OK) return s;
+  if (!aligned16(k) || !aligned16(kbar)) return MOBA_ERR_UNSUPPORTED;
+  DeviceState* st = nullptr;
+  if ((s = current_device(&st)) != MOBA_OK) return s;
+  hipError_t e = moba::launch_pool(k, is_f32, kbar, nullptr, N, H, D, B, stream);
+  return e == hipSuccess ? MOBA_OK : hip_fail(e);
+}
+
+int gate_impl(const void* q, const void* k, int32_t* sel, int64_t N, int32_t H, int32_t D, int32_t B, int32_t topk,
+              hipStream_t stream, bool is_f32) {
+  if (q == nullptr || k == nullptr || sel == nullptr) return MOBA_ERR_INVALID_ARG;
+  int s = check_shape(N, H, D, B);
+  if (s != MOBA_OK) return s;
+  if ((s = check_topk(N, B, topk)) != MOBA_OK) return s;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(sel)) return MOBA_ERR_UNSUPPORTED;
+  DeviceState* st = nullptr;
+  if ((s = current_device(&st)) != MOBA_OK) return s;
+  const moba::Problem p = make_problem(N, H, D, B, topk, is_f32);
+  const WsPlan w = plan(p, false);
+  char* base = nullptr;
+  if ((s = alloc_ws(st, w.total, stream, &base)) != MOBA_OK) return s;
+  moba::Workspace ws = bind(w, base, false);
+  hipError_t e = moba::launch_pool(k, is_f32, ws.kbar, is_f32 ? nullptr : ws.kpieces, N, H, D, B, stream);
+  if (e == hipSuccess) e = moba::launch_gate(p, q, ws, sel, false, stream);
+  return finish(e, base, stream);
+}
+
+int prefill_impl(const void* q, const void* k, const void* v, void* out, float* lse, int64_t N, int32_t H, int32_t D,
+                 int32_t B, int32_t topk, hipStream_t stream, bool is_f32) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || lse == nullptr) return MOBA_ERR_INVALID_ARG;
+  int s = check_shape(N, H, D, B);
+  if (s != MOBA_OK) return s;
+  if ((s = check_topk(N, B, topk)) != MOBA_OK) return s;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
+    return MOBA_ERR_UNSUPPORTED;
+  const moba::Problem p = make_problem(N, H, D, B, topk, is_f32);
+  if (p.p_off >= (int64_t{1} << 31)) return MOBA_ERR_UNSUPPORTED;
+  DeviceState* st = nullptr;
+  if ((s = current_device(&st)) != MOBA_OK) return s;
+  const WsPlan w = plan(p, true);
+  char* base = nullptr;
+  if ((s = alloc_ws(st, w.total, stream, &base)) != MOBA_OK) return s;
+  moba::Workspace ws = bind(w, base, true);
+  hipError_t e = moba::launch_pool(k, is_f32, ws.kbar, is_f32 ? nullptr : ws.kpieces, N, H, D, B, stream);
+  if (e == hipSuccess) e = moba::launch_gate(p, q, ws, ws.sel, true, stream);
+  if (e == hipSuccess) e = moba::launch_csr(p, ws, ws.sel, stream);
+  if (e == hipSuccess) e = moba::launch_attention(p, q, k, v, ws, st->num_cus, stream);
+  if (e == hipSuccess) e = moba::launch_merge(p, ws, out, lse, stream);
+  return finish(e, base, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moba_block_mean_keys(const void* k, float* kbar, int64_t N, int32_t H, int32_t D, int32_t block_size,
+                         hipStream_t stream) {
+  return block_mean_keys_impl(k, kbar, N, H, D, block_size, stream, false);
+}
+
+int moba_block_mean_keys_f32(const float* k, float* kbar, int64_t N, int32_t H, int32_t D, int32_t block_size,
+                             hipStream_t stream) {
+  return block_mean_keys_impl(k, kbar, N, H, D, block_size, stream, true);
+}
+
+int moba_gate_topk(const void* q, const void* k, int32_t* sel, int64_t N, int32_t H, int32_t D, int32_t block_size,
+                   int32_t topk, hipStream_t stream) {
+  return gate_impl(q, k, sel, N, H, D, block_size, topk, stream, false);
+}
+
+int moba_gate_topk_f32(const float* q, const float* k, int32_t* sel, int64_t N, int32_t H, int32_t D,
+                       int32_t block_size, int32_t topk, hipStream_t stream) {
+  return gate_impl(q, k, sel, N, H, D, block_size, topk, stream, true);
+}
+
+int moba_prefill_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int64_t N, int32_t H,
+                     int32_t D, int32_t block_size, int32_t topk, hipStream_t stream) {
+  return prefill_impl(q, k, v, out, lse, N, H, D, block_size, topk, stream, false);
+}
+
+int moba_prefill_fwd_f32(const float* q, const float* k, const float* v, float* out, float* lse, int64_t N, int32_t H,
+                         int32_t D, int32_t block_size, int32_t topk, hipStream_t stream) {
+  return prefill_impl(q, k, v, out, lse, N, H, D, block_size, topk, stream, true);
+}
+
+const char* moba_status_string(int status) {
+  switch (status) {
+    case MOBA_OK: return "MOBA_OK";
+    case MOBA_ERR_INVALID_ARG: return "MOBA_ERR_INVALID_ARG";
+    case MOBA_ERR_UNSUPPORTED: return "MOBA_ERR_UNSUPPORTED";
+    case MOBA_ERR_HIP: return "MOBA_ERR_HIP";
+    case MOBA_ERR_OUT_OF_MEMORY: return "MOBA_ERR_OUT_OF_MEMORY";
+    default: return "MOBA_ERR_UNKNOWN";
+  }
+}
+
+int moba_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

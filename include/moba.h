@@ -1,0 +1,131 @@
+/*
+ * libmoba — MoBA (Mixture of Block Attention) causal prefill forward pass for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (Moonshot AI's MoBA as described by the pomoai MoBA overview,
+ * "核心原理" steps 1-3, and by the 智东西 report, section 二):
+ *   - the N-token context is cut into n = N / block_size blocks of
+ *     block_size contiguous tokens;
+ *   - every query t in block j = t / block_size scores each past block i < j by
+ *     the dot product of q_t with the block's mean key (no parameters, no scale);
+ *   - it keeps its own block j (causally masked inside the block) plus the
+ *     topk - 1 best-scoring past blocks; a future block is never chosen;
+ *   - it attends, softmax(q k^T / sqrt(D)) v, over the union of those blocks
+ *     only; per-block partial outputs are merged by log-sum-exp weighting.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *   One sequence (batch 1), H query heads and H key/value heads.
+ *   q, k, v, out : device pointers, row-major [N][H][D] (token, head, dim),
+ *                  bf16 for the plain entry points and fp32 for the *_f32 twins.
+ *   lse          : device pointer, fp32 [H][N], natural log of the softmax
+ *                  denominator sum_s exp(q_t . k_s / sqrt(D)) over the attended keys.
+ *   sel          : device pointer, int32 [H][N][topk], chosen blocks of every
+ *                  (head, query) in ascending order, padded with -1 when the
+ *                  query has fewer than topk eligible blocks (j + 1 < topk).
+ *   kbar         : device pointer, fp32 [H][n][D], block mean keys.
+ *   topk         : blocks per query including the forced current block;
+ *                  topk >= n selects every past block (full causal attention).
+ *   stream       : HIP stream the work is enqueued on (0 = the null stream).
+ *   Selection ties (equal fp32 scores) go to the lower block index.
+ *
+ * Ownership and synchronisation: the caller owns every pointer argument. The
+ * library never frees or retains them. Temporary device workspace is taken
+ * from a library-owned stream-ordered memory pool on `stream` and returned to
+ * it on the same stream. Every call returns once its kernels are enqueued; it
+ * performs no host synchronisation. Device faults surface at the caller's next
+ * synchronisation, as for any HIP launch.
+ *
+ * Errors: arguments are checked before any HIP call or enqueue, and on an
+ * argument error nothing is written.
+ *   MOBA_ERR_INVALID_ARG   null pointer, N < 1, H < 1, topk < 1,
+ *                          block_size < 1, or block_size not dividing N.
+ *   MOBA_ERR_UNSUPPORTED   D not 64 or 128, block_size not a multiple of 64,
+ *                          a pointer not 16-byte aligned, more than
+ *                          MOBA_MAX_BLOCKS blocks, topk in (MOBA_MAX_TOPK, n),
+ *                          N >= 2^28, or a device that is not gfx950.
+ *   MOBA_ERR_HIP           a HIP runtime call or launch failed; the HIP error
+ *                          code is kept per thread (moba_last_hip_error).
+ *   MOBA_ERR_OUT_OF_MEMORY the workspace could not be allocated.
+ *
+ * Reentrancy: calls on different streams may run concurrently; the only
+ * process-wide state is a per-device cache of device properties and memory
+ * pools, created once. Results are bitwise deterministic (no floating-point
+ * atomics).
+ */
+#ifndef MOBA_H
+#define MOBA_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOBA_MAX_TOPK 32      /* largest ranked topk when topk < n */
+#define MOBA_MAX_BLOCKS 4096  /* largest n = N / block_size */
+
+typedef enum {
+  MOBA_OK = 0,
+  MOBA_ERR_INVALID_ARG = 1,
+  MOBA_ERR_UNSUPPORTED = 2,
+  MOBA_ERR_HIP = 3,
+  MOBA_ERR_OUT_OF_MEMORY = 4
+} moba_status;
+
+/*
+ * Block mean keys: kbar[h][i][:] = (1/block_size) * sum of k[t][h][:] over the
+ * block_size tokens t of block i, rounded once to fp32 (the sum is formed in
+ * fp64 in a fixed order, so the result is the correctly rounded mean whenever
+ * that sum is exact). Mean pooling of each block's keys is the gate's
+ * "representative vector" (wzjinhao.cn MoBA article, section 3, score_pooling
+ * = mean; 0539edu.com NSA/MoBA explainer, section 1).
+ * k: bf16 [N][H][D]; kbar: fp32 [H][n][D].
+ */
+int moba_block_mean_keys(const void* k, float* kbar, int64_t N, int32_t H, int32_t D,
+                         int32_t block_size, hipStream_t stream);
+int moba_block_mean_keys_f32(const float* k, float* kbar, int64_t N, int32_t H, int32_t D,
+                             int32_t block_size, hipStream_t stream);
+
+/*
+ * Gate and causal top-k only: writes sel (see conventions). The gate score of
+ * past block i for query t is the fp32 dot product <q_t, kbar_i> with kbar the
+ * fp32 block mean; future blocks are never scored and the current block is
+ * always chosen (wzjinhao.cn MoBA article, section 3, causal_mask and
+ * current_block_force; 智东西 report, section 二, gating and causality).
+ * q, k: bf16 [N][H][D] (fp32 for the _f32 twin); sel: int32 [H][N][topk].
+ */
+int moba_gate_topk(const void* q, const void* k, int32_t* sel, int64_t N, int32_t H, int32_t D,
+                   int32_t block_size, int32_t topk, hipStream_t stream);
+int moba_gate_topk_f32(const float* q, const float* k, int32_t* sel, int64_t N, int32_t H,
+                       int32_t D, int32_t block_size, int32_t topk, hipStream_t stream);
+
+/*
+ * Full MoBA causal prefill: out[t][h][:] = softmax over the attended keys of
+ * q_t . k_s / sqrt(D), applied to v, where the attended keys are every key of
+ * the chosen past blocks and the keys of the own block up to t itself; lse as
+ * in the conventions. Implements the five steps of the 智东西 report, section
+ * 二 (assign blocks, regroup queries by block, block attention, scatter back,
+ * online-softmax combination) with the attention formula of the 0539edu.com
+ * explainer, section 1.
+ * q, k, v, out: bf16 [N][H][D] (fp32 for the _f32 twin); lse: fp32 [H][N].
+ */
+int moba_prefill_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int64_t N, int32_t H, int32_t D, int32_t block_size, int32_t topk,
+                     hipStream_t stream);
+int moba_prefill_fwd_f32(const float* q, const float* k, const float* v, float* out, float* lse,
+                         int64_t N, int32_t H, int32_t D, int32_t block_size, int32_t topk,
+                         hipStream_t stream);
+
+/* Static, NUL-terminated name of a status code ("MOBA_OK", ...). */
+const char* moba_status_string(int status);
+
+/* hipError_t behind the calling thread's last MOBA_ERR_HIP (0 if none). */
+int moba_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOBA_H */

@@ -159,63 +159,130 @@ def _softmax_rows(logits: np.ndarray):
     return p / l, (m + np.log(l))[..., 0]
 
 
-def moba_ref(q, k, v, block_size: int, topk: int, sel=None, rows=None, max_rows_chunk: int = 512):
+def _attend_dense(q, k, v, block_size, sel, rows, out, lse, scale, max_rows_chunk):
+    """Dense masked form: per query block j, logits against every key of blocks
+    0..j, masked to A(t), softmax, then the product with V."""
+    N, H, D = q.shape
+    n = N // block_size
+    B = block_size
+    for h in range(H):
+        for j in range(n):
+            in_j = np.nonzero(rows // B == j)[0]          # indices into rows
+            if in_j.size == 0:
+                continue
+            nk = (j + 1) * B
+            kh = np.asarray(k[:nk, h, :], np.float64)
+            vh = np.asarray(v[:nk, h, :], np.float64)
+            key_block = np.arange(nk) // B
+            key_pos = np.arange(nk)
+            for c0 in range(0, in_j.size, max_rows_chunk):
+                idx = in_j[c0:c0 + max_rows_chunk]
+                t = rows[idx]
+                chosen = np.zeros((idx.size, n), dtype=bool)
+                for i, r in enumerate(idx):
+                    srow = sel[h, r]
+                    chosen[i, srow[srow >= 0]] = True
+                mask = chosen[:, key_block] & (key_pos[None, :] <= t[:, None])
+                logits = (np.asarray(q[t, h, :], np.float64) @ kh.T) * scale
+                logits = np.where(mask, logits, -np.inf)
+                p, l = _softmax_rows(logits)
+                out[idx, h] = p @ vh
+                lse[h, idx] = l
+
+
+def _attend_by_block(q, k, v, block_size, sel, rows, out, lse, scale):
+    """Softmax over A(t) for selected rows, with the logits of each chosen
+    block formed by one matrix product over the rows that chose it: a first
+    pass takes the row maxima over A(t), a second the exponentials, their sum
+    and the weighted sum of V."""
+    N, H, D = q.shape
+    B = block_size
+    R = rows.shape[0]
+    jrow = rows // B
+    for h in range(H):
+        qh = np.asarray(q[rows, h, :], np.float64)
+        s = sel[h]                                        # [R, topk]
+        blocks = np.unique(s[s >= 0])
+        groups = []
+        for b in blocks:
+            ridx = np.nonzero((s == b).any(axis=1))[0]
+            own = jrow[ridx] == b                          # the row's own block: keys up to t
+            groups.append((int(b), ridx, own))
+
+        def logits_of(b, ridx, own, kb):
+            lg = (qh[ridx] @ kb.T) * scale
+            if own.any():
+                kpos = b * B + np.arange(B)
+                lg[own] = np.where(kpos[None, :] <= rows[ridx][own][:, None], lg[own], -np.inf)
+            return lg
+
+        m = np.full(R, -np.inf)
+        for b, ridx, own in groups:
+            kb = np.asarray(k[b * B:(b + 1) * B, h, :], np.float64)
+            m[ridx] = np.maximum(m[ridx], logits_of(b, ridx, own, kb).max(axis=1))
+        l = np.zeros(R)
+        acc = np.zeros((R, D))
+        for b, ridx, own in groups:
+            kb = np.asarray(k[b * B:(b + 1) * B, h, :], np.float64)
+            vb = np.asarray(v[b * B:(b + 1) * B, h, :], np.float64)
+            p = np.exp(logits_of(b, ridx, own, kb) - m[ridx][:, None])
+            l[ridx] += p.sum(axis=1)
+            acc[ridx] += p @ vb
+        out[:, h] = acc / l[:, None]
+        lse[h] = m + np.log(l)
+
+
+def _attend_rowwise(q, k, v, block_size, sel, rows, out, lse, scale):
+    """One query at a time over its gathered key set A(t)."""
+    N, H, D = q.shape
+    for h in range(H):
+        for i, t in enumerate(rows):
+            keys = attended_keys(sel[h, i], int(t), block_size)
+            kh = np.asarray(k[keys, h, :], np.float64)
+            vh = np.asarray(v[keys, h, :], np.float64)
+            logits = (kh @ np.asarray(q[t, h], np.float64)) * scale
+            p, l = _softmax_rows(logits[None, :])
+            out[i, h] = p[0] @ vh
+            lse[h, i] = l[0]
+
+
+def moba_ref(q, k, v, block_size: int, topk: int, sel=None, rows=None, method: str | None = None,
+             max_rows_chunk: int = 512):
     """fp64 MoBA causal prefill.
 
     Arguments are [N, H, D] arrays (float32 holding exact bf16 or fp32 values).
     ``sel`` optionally overrides the gate ([H, R, topk] int32 for the same rows).
-    ``rows`` selects query rows to evaluate (default: all, in the dense masked
-    form per query block; otherwise row by row).
+    ``rows`` selects the query rows to evaluate (default: all).
+    ``method`` picks one of three evaluations of the same softmax over A(t):
+    "dense" (masked logits against all keys up to the row's block; the default
+    for all rows), "blocks" (logits of each chosen block for the rows that
+    chose it; the default for sampled rows) or "rowwise" (gathered keys, one
+    row at a time).
 
     Returns ``(out, lse, sel)``: out [R, H, D] fp64, lse [H, R] fp64 (natural
     log), sel [H, R, topk] int32.
     """
     q = np.asarray(q)
     N, H, D = q.shape
-    n = n_blocks(N, block_size)
+    n_blocks(N, block_size)
+    all_rows = rows is None
+    rows = np.arange(N, dtype=np.int64) if all_rows else np.asarray(rows, np.int64)
     if sel is None:
-        sel, _ = select_blocks(q, k, block_size, topk, rows=rows)
+        sel, _ = select_blocks(q, k, block_size, topk, rows=None if all_rows else rows)
+    if method is None:
+        method = "dense" if all_rows else "blocks"
     scale = 1.0 / math.sqrt(D)
-    if rows is not None:
-        rows = np.asarray(rows, np.int64)
-        R = rows.shape[0]
-        out = np.zeros((R, H, D), np.float64)
-        lse = np.zeros((H, R), np.float64)
-        for h in range(H):
-            kh = np.asarray(k[:, h, :], np.float64)
-            vh = np.asarray(v[:, h, :], np.float64)
-            for i, t in enumerate(rows):
-                keys = attended_keys(sel[h, i], int(t), block_size)
-                logits = (kh[keys] @ np.asarray(q[t, h], np.float64)) * scale
-                p, l = _softmax_rows(logits[None, :])
-                out[i, h] = p[0] @ vh[keys]
-                lse[h, i] = l[0]
-        return out, lse, sel
-
-    out = np.zeros((N, H, D), np.float64)
-    lse = np.zeros((H, N), np.float64)
-    B = block_size
-    for h in range(H):
-        qh = np.asarray(q[:, h, :], np.float64)
-        kh = np.asarray(k[:, h, :], np.float64)
-        vh = np.asarray(v[:, h, :], np.float64)
-        for j in range(n):
-            nk = (j + 1) * B
-            key_block = np.arange(nk) // B
-            key_pos = np.arange(nk)
-            for r0 in range(j * B, (j + 1) * B, max_rows_chunk):
-                r1 = min(r0 + max_rows_chunk, (j + 1) * B)
-                t = np.arange(r0, r1)
-                chosen = np.zeros((r1 - r0, n), dtype=bool)
-                for i in range(r1 - r0):
-                    s = sel[h, r0 + i]
-                    chosen[i, s[s >= 0]] = True
-                mask = chosen[:, key_block] & (key_pos[None, :] <= t[:, None])
-                logits = (qh[r0:r1] @ kh[:nk].T) * scale
-                logits = np.where(mask, logits, -np.inf)
-                p, l = _softmax_rows(logits)
-                out[r0:r1, h] = p @ vh[:nk]
-                lse[h, r0:r1] = l
+    R = rows.shape[0]
+    out = np.zeros((R, H, D), np.float64)
+    lse = np.zeros((H, R), np.float64)
+    if method == "dense":
+        _attend_dense(q, k, v, block_size, sel, rows, out, lse, scale, max_rows_chunk)
+    elif method == "blocks":
+        _attend_by_block(q, k, v, block_size, sel, rows, out, lse, scale)
+    elif method == "rowwise":
+        _attend_rowwise(q, k, v, block_size, sel, rows, out, lse, scale)
+    else:
+        raise ValueError(method)
     return out, lse, sel
 
 

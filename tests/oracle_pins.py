@@ -318,15 +318,22 @@ def pin_gate_rounding(m):
 
 
 def pin_row_mode_matches(m):
-    """Row-by-row evaluation equals the dense masked evaluation."""
-    N, H, D, B, topk = 128, 2, 8, 16, 3
-    q, k, v = _rand(N, H, D, 151)
-    out, lse, sel = m.moba_ref(q, k, v, B, topk)
-    rows = np.array([0, 5, 16, 17, 63, 100, 127])
-    o2, l2, s2 = m.moba_ref(q, k, v, B, topk, rows=rows)
-    assert np.array_equal(s2, sel[:, rows])
-    assert np.allclose(o2, out[rows], atol=1e-13, rtol=0)
-    assert np.allclose(l2, lse[:, rows], atol=1e-13, rtol=0)
+    """The three evaluations of the softmax over A(t) agree: dense masked
+    logits, per-block logits over the rows that chose the block, and one
+    gathered row at a time."""
+    for N, H, D, B, topk, seed in [(128, 2, 8, 16, 3, 151), (192, 1, 8, 64, 2, 152), (96, 2, 4, 8, 20, 153)]:
+        q, k, v = _rand(N, H, D, seed)
+        out, lse, sel = m.moba_ref(q, k, v, B, topk)
+        rows = np.unique(np.array([0, 5, B - 1, B, B + 1, N // 2, N - 2, N - 1]))
+        for method in ("blocks", "rowwise", "dense"):
+            o2, l2, s2 = m.moba_ref(q, k, v, B, topk, rows=rows, method=method)
+            assert np.array_equal(s2, sel[:, rows])
+            assert np.allclose(o2, out[rows], atol=1e-13, rtol=0), method
+            assert np.allclose(l2, lse[:, rows], atol=1e-13, rtol=0), method
+        allrows = np.arange(N)
+        o3, l3, _ = m.moba_ref(q, k, v, B, topk, rows=allrows, method="blocks")
+        assert np.allclose(o3, out, atol=1e-13, rtol=0)
+        assert np.allclose(l3, lse, atol=1e-13, rtol=0)
 
 
 ALL_PINS = [

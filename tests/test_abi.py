@@ -1,0 +1,135 @@
+"""CPU tests of the C-ABI boundary: the library loads, exports every declared
+symbol, and rejects bad arguments before touching the GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_long_gating_amd as moba
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moba.h")
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moba_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moba.library_path()):
+        pytest.fail("libmoba.so is not built (run __graft_entry__.build())")
+    return moba.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("moba_gate_topk", "moba_prefill_fwd", "moba_gate_topk_f32", "moba_prefill_fwd_f32",
+              "moba_block_mean_keys", "moba_block_mean_keys_f32", "moba_status_string", "moba_last_hip_error"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(moba.library_path())
+    for name in declared_functions():
+        assert hasattr(raw, name), f"{name} declared in moba.h but not exported"
+
+
+def test_binding_covers_every_symbol():
+    assert set(declared_functions()) == set(moba._SIGNATURES)
+
+
+def test_header_constants_match_binding():
+    src = open(HEADER).read()
+    assert int(re.search(r"#define MOBA_MAX_TOPK (\d+)", src).group(1)) == moba.MAX_TOPK
+    assert int(re.search(r"#define MOBA_MAX_BLOCKS (\d+)", src).group(1)) == moba.MAX_BLOCKS
+    for code, name in moba.STATUS.items():
+        assert re.search(rf"{name} = {code}\b", src)
+
+
+def test_status_strings(lib):
+    for code, name in moba.STATUS.items():
+        assert lib.moba_status_string(code).decode() == name
+    assert lib.moba_status_string(99).decode() == "MOBA_ERR_UNKNOWN"
+    assert lib.moba_last_hip_error() == 0
+
+
+# Fake, never dereferenced, 16-byte aligned addresses: every call below must be
+# rejected by the host-side checks before any HIP call.
+A = 0x10000
+
+
+def prefill(lib, N=1024, H=1, D=128, B=128, topk=3, ptrs=(A, A, A, A, A), f32=False):
+    fn = lib.moba_prefill_fwd_f32 if f32 else lib.moba_prefill_fwd
+    return fn(*ptrs, N, H, D, B, topk, None)
+
+
+def gate(lib, N=1024, H=1, D=128, B=128, topk=3, ptrs=(A, A, A), f32=False):
+    fn = lib.moba_gate_topk_f32 if f32 else lib.moba_gate_topk
+    return fn(*ptrs, N, H, D, B, topk, None)
+
+
+def pool(lib, N=1024, H=1, D=128, B=128, ptrs=(A, A), f32=False):
+    fn = lib.moba_block_mean_keys_f32 if f32 else lib.moba_block_mean_keys
+    return fn(*ptrs, N, H, D, B, None)
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_null_pointers(lib, f32):
+    for i in range(5):
+        ptrs = [A] * 5
+        ptrs[i] = None
+        assert prefill(lib, ptrs=tuple(ptrs), f32=f32) == INVALID
+    for i in range(3):
+        ptrs = [A] * 3
+        ptrs[i] = None
+        assert gate(lib, ptrs=tuple(ptrs), f32=f32) == INVALID
+    assert pool(lib, ptrs=(None, A), f32=f32) == INVALID
+    assert pool(lib, ptrs=(A, None), f32=f32) == INVALID
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_invalid_shapes(lib, f32):
+    for kw in (dict(N=0), dict(N=-5), dict(H=0), dict(topk=0), dict(topk=-1), dict(B=0),
+               dict(N=1000, B=128), dict(N=1024, B=384)):
+        assert prefill(lib, f32=f32, **kw) == INVALID, kw
+        assert gate(lib, f32=f32, **kw) == INVALID, kw
+    assert pool(lib, N=1000, B=128, f32=f32) == INVALID
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_unsupported_shapes(lib, f32):
+    for kw in (dict(D=96), dict(D=256), dict(D=32), dict(N=960, B=96), dict(N=1 << 28, B=1 << 16),
+               dict(N=64 * 5000, B=64), dict(N=64 * 100, B=64, topk=33), dict(H=70000)):
+        assert prefill(lib, f32=f32, **kw) == UNSUPPORTED, kw
+        assert gate(lib, f32=f32, **kw) == UNSUPPORTED, kw
+    for i in range(5):
+        ptrs = [A] * 5
+        ptrs[i] = A + 4
+        assert prefill(lib, ptrs=tuple(ptrs), f32=f32) == UNSUPPORTED
+    assert gate(lib, ptrs=(A, A, A + 8), f32=f32) == UNSUPPORTED
+    assert pool(lib, D=80, f32=f32) == UNSUPPORTED
+
+
+def test_topk_at_least_n_is_not_limited(lib):
+    # n = 100 blocks, topk >= n selects everything and is accepted by the checks
+    # (it then needs a device, which this test does not reach: an invalid H stops it)
+    assert prefill(lib, N=6400, B=64, topk=150, H=0) == INVALID
+    assert prefill(lib, N=6400, B=64, topk=50) == UNSUPPORTED
+
+
+def test_python_binding_rejects_bad_tensors():
+    import torch
+    q = torch.zeros(64, 1, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        moba.prefill(q, q, q, 64, 3)          # not on a GPU
+    with pytest.raises(TypeError):
+        moba.prefill(q.half(), q.half(), q.half(), 64, 3)
+    with pytest.raises(ValueError):
+        moba.gate_topk(q[0], q[0], 64, 3)

@@ -1,0 +1,184 @@
+"""GPU parity: the HIP path through the C-ABI against the fp64 oracle.
+
+Selections must match the oracle bit for bit except on near-ties (see
+tests/parity.py); outputs must stay within max-abs tolerances: 2e-2 (bf16 in,
+fp32 accumulate) and 1e-4 (fp32 in); lse within 1e-2 / 1e-5.
+"""
+
+import numpy as np
+import pytest
+
+from block_sparse_long_gating_amd import synth
+from tests.parity import LSE_TOL, OUT_TOL, compare_selection, log, max_abs, to_device
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moba():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import block_sparse_long_gating_amd as m
+    m.load_library()
+    return m
+
+
+# (N, H, D, B, topk, dtype, seed): several gate tiles and work items, ragged
+# query lists, B = 64 (a gate tile spans two blocks), N % 128 != 0, n = 1,
+# topk = 1, topk >= n (full causal attention), D = 64.
+SMALL = [
+    (2048, 2, 128, 256, 3, "bf16", 1),
+    (1536, 3, 128, 128, 4, "bf16", 2),
+    (4096, 1, 64, 512, 2, "bf16", 3),
+    (640, 2, 128, 64, 5, "bf16", 4),
+    (320, 1, 128, 64, 3, "bf16", 5),
+    (256, 2, 128, 256, 3, "bf16", 6),
+    (1024, 2, 128, 128, 1, "bf16", 7),
+    (1024, 1, 128, 128, 8, "bf16", 8),
+    (1024, 1, 128, 128, 20, "bf16", 9),
+    (2048, 1, 128, 64, 12, "bf16", 10),
+    (2048, 1, 64, 256, 3, "fp32", 11),
+    (1024, 2, 128, 128, 4, "fp32", 12),
+    (640, 1, 64, 64, 5, "fp32", 13),
+    (4096, 1, 128, 64, 32, "bf16", 14),
+]
+
+
+def _ids(c):
+    return "N{}_H{}_D{}_B{}_k{}_{}".format(*c[:6])
+
+
+def run_case(moba, q, k, v, B, topk, dtype, rows=None, full_out=True):
+    from oracle import moba_ref, pooled_keys_fp32, select_blocks
+    N, H, D = q.shape
+    qd, kd, vd = (to_device(x, dtype) for x in (q, k, v))
+    log(f"  gpu: block_mean_keys N={N} H={H} D={D} B={B}")
+    kbar = moba.block_mean_keys(kd, B)
+    log(f"  gpu: gate_topk topk={topk}")
+    sel = moba.gate_topk(qd, kd, B, topk)
+    log(f"  gpu: prefill")
+    out, lse = moba.prefill(qd, kd, vd, B, topk)
+    torch.cuda.synchronize()
+    log("  gpu: done")
+
+    ref_kbar = pooled_keys_fp32(k, B)
+    kb = kbar.cpu().numpy()
+    assert np.max(np.abs(kb - ref_kbar) / np.maximum(np.abs(ref_kbar), 1e-30)) <= 1e-6
+    kbar_exact = float(np.mean(kb == ref_kbar))
+
+    gsel = sel.cpu().numpy()
+    ref_sel, _ = select_blocks(q, k, B, topk)
+    cmp = compare_selection(gsel, ref_sel, q, k, B, topk)
+    assert not cmp["bad"], f"selection mismatches beyond near-ties: {cmp['bad'][:5]}"
+
+    if rows is None:
+        rows = np.arange(N)
+    rows = np.asarray(rows)
+    method = "dense" if (full_out and N * H <= 8192) else "blocks"
+    ref_out, ref_lse, _ = moba_ref(q, k, v, B, topk, sel=gsel[:, rows], rows=rows, method=method)
+    got_out = out.float().cpu().numpy()[rows]
+    got_lse = lse.cpu().numpy()[:, rows]
+    e_out, e_lse = max_abs(got_out, ref_out), max_abs(got_lse, ref_lse)
+    log(f"  sel mismatch rows {cmp['mismatch']} (exempt {cmp['exempt']}), kbar bit-exact {kbar_exact:.4f}, "
+        f"max|out| err {e_out:.3e}, max|lse| err {e_lse:.3e}")
+    assert e_out <= OUT_TOL[dtype], e_out
+    assert e_lse <= LSE_TOL[dtype], e_lse
+    assert np.all(np.isfinite(got_out))
+    return out, lse, sel
+
+
+@pytest.mark.parametrize("case", SMALL, ids=_ids)
+def test_prefill_small(moba, case):
+    N, H, D, B, topk, dtype, seed = case
+    log(f"case {_ids(case)}")
+    q, k, v = synth.make_qkv(N, H, D, seed=[100, seed], dtype=dtype)
+    run_case(moba, q, k, v, B, topk, dtype)
+
+
+def test_structured_inputs(moba):
+    """Zero queries (every gate score ties: the lower-index rule decides) and
+    constant values (the output is that constant)."""
+    N, H, D, B, topk = 1024, 2, 128, 128, 3
+    q, k, v = synth.make_qkv(N, H, D, seed=[101, 0], dtype="bf16")
+    q0 = np.zeros_like(q)
+    log("case zero-q")
+    _, _, sel = run_case(moba, q0, k, v, B, topk, "bf16")
+    s = sel.cpu().numpy()
+    for t in range(B * 3, N, 97):
+        j = t // B
+        assert list(s[0, t]) == [0, 1, j]
+    vc = np.broadcast_to(synth.round_to_bf16(np.linspace(-2, 2, D, dtype=np.float32)), (N, H, D)).copy()
+    log("case constant-v")
+    out, _, _ = run_case(moba, q, k, vc, B, topk, "bf16")
+    assert max_abs(out.float().cpu().numpy(), vc) <= 2e-2
+
+
+WORKLOAD_ROWS = {"tiny": None, "c32k": None, "h32": 4096, "n128k": 4096, "m1": 4096}
+
+
+@pytest.mark.parametrize("name", list(WORKLOAD_ROWS))
+def test_workload(moba, name):
+    log(f"workload {name}")
+    w, q, k, v = synth.make_workload(name)
+    count = WORKLOAD_ROWS[name]
+    rows = None if count is None else synth.sample_rows(w.N, count, synth.SAMPLE_SEED[name])
+    run_case(moba, q, k, v, w.block_size, w.topk, w.dtype, rows=rows, full_out=(count is None))
+
+
+def test_needles_are_found(moba):
+    """The planted needle blocks of the 128K workload are chosen far more often
+    than an average past block."""
+    w, q, k, v, ex = synth.make_workload("n128k", with_extras=True)
+    sel = moba.gate_topk(to_device(q, "bf16"), to_device(k, "bf16"), w.block_size, w.topk).cpu().numpy()
+    base = (w.topk - 1) / (w.n_blocks - 1)
+    for h, needles in enumerate(ex["needle_blocks"]):
+        late = sel[h, (w.n_blocks - 1) * w.block_size:]
+        hits = float(np.isin(late, needles).sum()) / (late.shape[0] * len(needles))
+        log(f"  head {h}: needle hit rate {hits:.3f} vs average past block {base:.3f}")
+        assert hits > base, (h, hits, base)
+
+
+def test_deterministic(moba):
+    N, H, D, B, topk = 4096, 4, 128, 256, 4
+    q, k, v = synth.make_qkv(N, H, D, seed=[102, 0], dtype="bf16")
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    o1, l1 = moba.prefill(qd, kd, vd, B, topk)
+    o2, l2 = moba.prefill(qd, kd, vd, B, topk)
+    s1 = moba.gate_topk(qd, kd, B, topk)
+    s2 = moba.gate_topk(qd, kd, B, topk)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+    assert torch.equal(s1, s2)
+
+
+def test_bad_arguments_leave_outputs_untouched(moba):
+    N, H, D = 1024, 1, 128
+    q = torch.zeros(N, H, D, dtype=torch.bfloat16, device="cuda")
+    out = torch.full_like(q, 7.0)
+    lse = torch.full((H, N), 5.0, device="cuda")
+    with pytest.raises(moba.MobaError) as e:
+        moba.prefill(q, q, q, 100, 3, out=out, lse=lse)     # block size does not divide N
+    assert e.value.status == 1
+    with pytest.raises(moba.MobaError) as e:
+        moba.prefill(q, q, q, 96, 3, out=out, lse=lse)      # block size not a multiple of 64
+    assert e.value.status == 2
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all()) and bool((lse == 5.0).all())
+
+
+def test_streams(moba):
+    """Work is enqueued on the caller's current stream."""
+    N, H, D, B, topk = 2048, 2, 128, 256, 3
+    q, k, v = synth.make_qkv(N, H, D, seed=[103, 0], dtype="bf16")
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    ref_o, ref_l = moba.prefill(qd, kd, vd, B, topk)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, l = moba.prefill(qd, kd, vd, B, topk)
+    s.synchronize()
+    assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16))
+    assert torch.equal(l, ref_l)

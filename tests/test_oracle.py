@@ -49,6 +49,11 @@ MUTATIONS = {
     "transposed_scores": ("s = np.asarray(q_rows, np.float64) @ np.asarray(kbar32_h, np.float64).T",
                           "s = (np.asarray(q_rows, np.float64)[:, ::-1] @ np.asarray(kbar32_h, np.float64).T)"),
     "softmax_without_max": ("p = np.exp(logits - m)", "p = np.exp(logits - m * 0.5)"),
+    "blocks_causal_off_by_one": ("lg[own] = np.where(kpos[None, :] <= rows[ridx][own][:, None], lg[own], -np.inf)",
+                                 "lg[own] = np.where(kpos[None, :] < rows[ridx][own][:, None], lg[own], -np.inf)"),
+    "blocks_drops_denominator_terms": ("l[ridx] += p.sum(axis=1)", "l[ridx] = p.sum(axis=1)"),
+    "rowwise_wrong_head": ("kh = np.asarray(k[keys, h, :], np.float64)",
+                           "kh = np.asarray(k[keys, (h + 1) % H, :], np.float64)"),
 }
 
 
