@@ -1,0 +1,240 @@
+"""Benchmark of the MoBA causal prefill on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload h32]
+
+One step is one whole ``moba_prefill_fwd`` call (block mean-pool, gate and
+causal top-k, query lists, block attention, LSE merge) on inputs already
+resident in HBM, including the workspace taken from the library's stream-ordered
+pool. Prints one JSON line with the effective TFLOP/s (only the attended,
+causal (query, key) pairs of the selected blocks count, 4*D FLOPs each), the
+fraction of the bf16 MFMA peak, per-stage device times from HIP events the
+library records on its stream, the roofline of the dominant kernel (block
+attention), and the fp64 oracle timed on the host on a sample of query rows.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoBA prefill effective TFLOP/s + % bf16 MFMA peak at 32K/B512/top-3, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X published dense bf16 MFMA peak
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_h32_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "block_sparse_long_gating_amd", "csrc", "attn.hip")
+
+
+def effective_pairs(N: int, B: int, topk: int) -> int:
+    """Attended (query, key) pairs of one head: every row of block j sees
+    min(topk-1, j) past blocks in full and its own block up to itself."""
+    n = N // B
+    return sum(B * B * min(topk - 1, j) + B * (B + 1) // 2 for j in range(n))
+
+
+def row_pairs(rows: np.ndarray, B: int, topk: int) -> int:
+    j = rows // B
+    return int(np.sum(np.minimum(topk - 1, j) * B + rows % B + 1))
+
+
+def device_info():
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "cus": p.multi_processor_count, "arch": getattr(p, "gcnArchName", "")}
+    try:
+        import ctypes
+        hip = ctypes.CDLL("libamdhip64.so")
+        clk = ctypes.c_int()
+        # hipDeviceAttributeClockRate (kHz)
+        if hip.hipDeviceGetAttribute(ctypes.byref(clk), 5, 0) == 0 and clk.value > 0:
+            info["clock_mhz"] = clk.value / 1000.0
+    except OSError:
+        pass
+    return info
+
+
+def traffic_for(ms_attn_per_call: float):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, if it was taken with the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    src_hash = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    if t.get("attn_source_sha256") != src_hash:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, gpu_out, gpu_lse, target_s: float):
+    """The fp64 oracle as it stands, on a seeded sample of query rows."""
+    import threadpoolctl
+
+    from block_sparse_long_gating_amd import synth
+    from oracle import moba_ref
+
+    cores = len(os.sched_getaffinity(0))
+    blas = threadpoolctl.threadpool_info()
+    threads = max([b.get("num_threads", 1) for b in blas] + [1])
+    R = min(1024, w.N)
+    while True:
+        rows = synth.sample_rows(w.N, R, 2000 + R)
+        t0 = time.perf_counter()
+        out, lse, sel = moba_ref(q, k, v, w.block_size, w.topk, rows=rows)
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 3 or R >= w.N:
+            break
+        R = min(w.N, int(R * max(2.0, target_s / max(dt, 1e-3))))
+    flops = 4.0 * w.D * w.H * row_pairs(rows, w.block_size, w.topk)
+    res = {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{R} seeded query rows x {w.H} heads of the {w.name} workload "
+                  f"(gate over all blocks + fp64 softmax over the attended keys); {dt:.2f} s; "
+                  f"{cores} cores visible, BLAS threads {threads}",
+        "seconds": dt,
+        "rows": int(R),
+    }
+    got = gpu_out[rows].astype(np.float64)
+    res_parity = {
+        "rows": int(R),
+        "max_abs_out": float(np.max(np.abs(got - out))),
+        "max_abs_lse": float(np.max(np.abs(gpu_lse[:, rows] - lse))),
+    }
+    return res, res_parity
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="h32")
+    ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="after timing, run plain device copies of this size (HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by head with no communication; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_sparse_long_gating_amd as moba
+    from block_sparse_long_gating_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    moba.load_library()
+    w, q, k, v = synth.make_workload(args.workload)
+    if w.dtype != "bf16":
+        print("bench.py times the bf16 path", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+
+    def up(x):
+        return torch.from_numpy(synth.bf16_bits(x)).view(torch.bfloat16).to(dev)
+
+    qd, kd, vd = up(q), up(k), up(v)
+    out = torch.empty_like(qd)
+    lse = torch.empty((w.H, w.N), dtype=torch.float32, device=dev)
+    print(f"[bench] workload {w.name}: {w.description}", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        moba.prefill(qd, kd, vd, w.block_size, w.topk, out=out, lse=lse)
+    torch.cuda.synchronize()
+
+    events = [moba.StageEvents() for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        moba.prefill(qd, kd, vd, w.block_size, w.topk, out=out, lse=lse, events=events[i])
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    for e in events:
+        e.accumulate()
+    stage_ms = {s: sum(e.totals[s] for e in events) / args.steps for s in moba.STAGES}
+    for e in events:
+        e.close()
+    ms = total_ms / args.steps
+    print(f"[bench] {args.steps} steps, {ms:.3f} ms/step, stages (us): "
+          + ", ".join(f"{s} {1e3 * t:.1f}" for s, t in stage_ms.items()), file=sys.stderr, flush=True)
+
+    if args.calibrate_copy_mib > 0:
+        nbytes = args.calibrate_copy_mib << 20
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    pairs = effective_pairs(w.N, w.block_size, w.topk) * w.H
+    flops = 4.0 * w.D * pairs
+    tflops = flops / (ms * 1e-3) / 1e12
+    attn_ms = stage_ms["attention"]
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    info = device_info()
+
+    result = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "N": w.N, "H": w.H, "D": w.D, "block_size": w.block_size,
+                   "top_k": w.topk, "batch": 1, "inputs": w.description},
+        "pct_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "effective_gflop": flops / 1e9,
+        "stages_us": {s: 1e3 * t for s, t in stage_ms.items()},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_bf16_kernel (block attention)",
+            "achieved": attn_tflops,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": attn_tflops / PEAK_BF16_TFLOPS,
+            "traffic": traffic_for(attn_ms),
+        },
+        "device": info,
+    }
+
+    if args.cpu_baseline == "on":
+        torch.cuda.synchronize()
+        got_out = out.float().cpu().numpy()
+        got_lse = lse.cpu().numpy()
+        cb, parity = cpu_baseline(w, q, k, v, got_out, got_lse, args.cpu_seconds)
+        result["cpu_baseline"] = {kk: cb[kk] for kk in ("value", "unit", "cores", "kind", "sample")}
+        result["parity_sample"] = parity
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -15,7 +15,7 @@ import ctypes
 import os
 
 __all__ = ["prefill", "gate_topk", "block_mean_keys", "MobaError", "library_path", "load_library",
-           "STATUS", "MAX_TOPK", "MAX_BLOCKS"]
+           "StageEvents", "STAGES", "STATUS", "MAX_TOPK", "MAX_BLOCKS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmoba.so")
@@ -37,6 +37,7 @@ _SIGNATURES = {
     "moba_gate_topk_f32": [_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P],
     "moba_prefill_fwd": [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P],
     "moba_prefill_fwd_f32": [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P],
+    "moba_prefill_fwd_timed": [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P],
     "moba_status_string": [ctypes.c_int],
     "moba_last_hip_error": [],
 }
@@ -122,8 +123,51 @@ def gate_topk(q, k, block_size: int, topk: int):
     return sel
 
 
-def prefill(q, k, v, block_size: int, topk: int, out=None, lse=None):
-    """MoBA causal prefill. Returns ``(out [N,H,D], lse [H,N] fp32)``."""
+STAGES = ("pool", "gate", "lists", "attention", "merge")
+STAGE_EVENTS = len(STAGES) + 1
+
+
+class StageEvents:
+    """HIP events the library records at its stage boundaries (bf16 prefill)."""
+
+    def __init__(self):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.array = (ctypes.c_void_p * STAGE_EVENTS)()
+        for i in range(STAGE_EVENTS):
+            ev = ctypes.c_void_p()
+            if self._hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.array[i] = ev
+        self.totals = {s: 0.0 for s in STAGES}
+        self.calls = 0
+
+    def accumulate(self):
+        """Wait for the last recorded call and add its stage times (ms)."""
+        if self._hip.hipEventSynchronize(self.array[STAGE_EVENTS - 1]) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        ms = ctypes.c_float()
+        for i, s in enumerate(STAGES):
+            if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.array[i], self.array[i + 1]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            self.totals[s] += ms.value
+        self.calls += 1
+
+    def mean_ms(self):
+        return {s: v / max(self.calls, 1) for s, v in self.totals.items()}
+
+    def close(self):
+        for i in range(STAGE_EVENTS):
+            self._hip.hipEventDestroy(self.array[i])
+
+
+def prefill(q, k, v, block_size: int, topk: int, out=None, lse=None, events: "StageEvents | None" = None):
+    """MoBA causal prefill. Returns ``(out [N,H,D], lse [H,N] fp32)``.
+
+    ``events`` (bf16 only) records the stage boundaries for timing."""
     import torch
     N, H, D, f32 = _check_qkv(q, k, v)
     lib = load_library()
@@ -135,6 +179,13 @@ def prefill(q, k, v, block_size: int, topk: int, out=None, lse=None):
         raise ValueError("out must be a contiguous tensor like q")
     if lse.shape != (H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous fp32 [H, N] tensor")
+    if events is not None:
+        if f32:
+            raise ValueError("stage events are recorded by the bf16 prefill only")
+        _check(lib.moba_prefill_fwd_timed(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                          N, H, D, block_size, topk, _stream(q.device), events.array),
+               "moba_prefill_fwd_timed")
+        return out, lse
     fn = lib.moba_prefill_fwd_f32 if f32 else lib.moba_prefill_fwd
     _check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), N, H, D, block_size, topk,
               _stream(q.device)), "moba_prefill_fwd")

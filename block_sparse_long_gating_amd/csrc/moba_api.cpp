@@ -227,7 +227,7 @@ int gate_impl(const void* q, const void* k, int32_t* sel, int64_t N, int32_t H, 
 }
 
 int prefill_impl(const void* q, const void* k, const void* v, void* out, float* lse, int64_t N, int32_t H, int32_t D,
-                 int32_t B, int32_t topk, hipStream_t stream, bool is_f32) {
+                 int32_t B, int32_t topk, hipStream_t stream, bool is_f32, hipEvent_t* events = nullptr) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || lse == nullptr) return MOBA_ERR_INVALID_ARG;
   int s = check_shape(N, H, D, B);
   if (s != MOBA_OK) return s;
@@ -242,11 +242,18 @@ int prefill_impl(const void* q, const void* k, const void* v, void* out, float* 
   char* base = nullptr;
   if ((s = alloc_ws(st, w.total, stream, &base)) != MOBA_OK) return s;
   moba::Workspace ws = bind(w, base, true);
-  hipError_t e = moba::launch_pool(k, is_f32, ws.kbar, is_f32 ? nullptr : ws.kpieces, N, H, D, B, stream);
+  auto mark = [&](int i) { return events ? hipEventRecord(events[i], stream) : hipSuccess; };
+  hipError_t e = mark(0);
+  if (e == hipSuccess) e = moba::launch_pool(k, is_f32, ws.kbar, is_f32 ? nullptr : ws.kpieces, N, H, D, B, stream);
+  if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) e = moba::launch_gate(p, q, ws, ws.sel, true, stream);
+  if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess) e = moba::launch_csr(p, ws, ws.sel, stream);
+  if (e == hipSuccess) e = mark(3);
   if (e == hipSuccess) e = moba::launch_attention(p, q, k, v, ws, st->num_cus, stream);
+  if (e == hipSuccess) e = mark(4);
   if (e == hipSuccess) e = moba::launch_merge(p, ws, out, lse, stream);
+  if (e == hipSuccess) e = mark(5);
   return finish(e, base, stream);
 }
 
@@ -277,6 +284,11 @@ int moba_gate_topk_f32(const float* q, const float* k, int32_t* sel, int64_t N, 
 int moba_prefill_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int64_t N, int32_t H,
                      int32_t D, int32_t block_size, int32_t topk, hipStream_t stream) {
   return prefill_impl(q, k, v, out, lse, N, H, D, block_size, topk, stream, false);
+}
+
+int moba_prefill_fwd_timed(const void* q, const void* k, const void* v, void* out, float* lse, int64_t N, int32_t H,
+                           int32_t D, int32_t block_size, int32_t topk, hipStream_t stream, hipEvent_t* events) {
+  return prefill_impl(q, k, v, out, lse, N, H, D, block_size, topk, stream, false, events);
 }
 
 int moba_prefill_fwd_f32(const float* q, const float* k, const float* v, float* out, float* lse, int64_t N, int32_t H,

@@ -118,6 +118,19 @@ int moba_prefill_fwd_f32(const float* q, const float* k, const float* v, float* 
                          int64_t N, int32_t H, int32_t D, int32_t block_size, int32_t topk,
                          hipStream_t stream);
 
+/*
+ * moba_prefill_fwd with stage timing: identical work and results, and, when
+ * `events` is not NULL, events[0..MOBA_STAGE_EVENTS-1] (created by the caller
+ * with hipEventCreate) are recorded on `stream` at the stage boundaries:
+ *   0 before the block mean-pool, 1 before the gate/top-k, 2 before the query
+ *   lists, 3 before the block attention, 4 before the merge, 5 after it.
+ * hipEventElapsedTime between neighbours gives each stage's device time.
+ */
+#define MOBA_STAGE_EVENTS 6
+int moba_prefill_fwd_timed(const void* q, const void* k, const void* v, void* out, float* lse,
+                           int64_t N, int32_t H, int32_t D, int32_t block_size, int32_t topk,
+                           hipStream_t stream, hipEvent_t* events);
+
 /* Static, NUL-terminated name of a status code ("MOBA_OK", ...). */
 const char* moba_status_string(int status);
 

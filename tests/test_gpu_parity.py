@@ -162,11 +162,15 @@ def test_bad_arguments_leave_outputs_untouched(moba):
     with pytest.raises(moba.MobaError) as e:
         moba.prefill(q, q, q, 100, 3, out=out, lse=lse)     # block size does not divide N
     assert e.value.status == 1
+    q2 = torch.zeros(960, H, D, dtype=torch.bfloat16, device="cuda")
+    out2 = torch.full_like(q2, 7.0)
+    lse2 = torch.full((H, 960), 5.0, device="cuda")
     with pytest.raises(moba.MobaError) as e:
-        moba.prefill(q, q, q, 96, 3, out=out, lse=lse)      # block size not a multiple of 64
+        moba.prefill(q2, q2, q2, 96, 3, out=out2, lse=lse2)  # block size not a multiple of 64
     assert e.value.status == 2
     torch.cuda.synchronize()
     assert bool((out == 7.0).all()) and bool((lse == 5.0).all())
+    assert bool((out2 == 7.0).all()) and bool((lse2 == 5.0).all())
 
 
 def test_streams(moba):
