@@ -13,15 +13,21 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-// Queries per gate tile and per attention work item (4 waves x 32 queries).
+// Queries per gate tile (4 waves x 32 queries).
 constexpr int kQTile = 128;
+// Queries per block-attention work item (4 waves x 64 queries).
+constexpr int kAttnTile = 256;
 // Keys per attention tile staged in LDS.
 constexpr int kKTile = 64;
 // Number of XCDs (L2 domains) of an MI355X; workgroups are dealt to them round-robin.
 constexpr int kXcds = 8;
+// Spacing (in int32) of the per-XCD work cursors: atomics from different XCDs
+// on one cache line serialise.
+constexpr int kCursorStride = 64;
+constexpr int kCounterInts = kCursorStride * (1 + kXcds);
 
 // One work item of the block-attention kernel over the off-diagonal (past block)
-// query lists: head h, key block b, and `count` (<= kQTile) consecutive entries
+// query lists: head h, key block b, and `count` (<= kAttnTile) consecutive entries
 // of the block's query list starting at global list position `start`.
 struct WorkItem {
   int32_t h;
@@ -41,7 +47,8 @@ struct Workspace {
   int32_t* qidx;        // [P_off] query of every list entry
   int32_t* inv;         // [H][N][Lmax] list position of each off-diagonal selection
   WorkItem* items;      // [max_items]
-  int32_t* counters;    // [0]: number of off-diagonal items, [8..15]: per-XCD item cursors
+  int32_t* counters;    // [0]: number of off-diagonal items; per-XCD item cursors at
+                        // [kCursorStride * (1 + x)], one cache line apart
   void* part_diag;      // [H][N][D] own-block partial outputs (bf16 or fp32)
   float* lse_diag;      // [H][N]
   void* part_off;       // [P_off][D] past-block partial outputs

@@ -7,7 +7,7 @@
 //   1. scan_tiles: per (head, block), exclusive prefix of the per-tile counts
 //      written by the gate, and the list length;
 //   2. build_lists (one workgroup): global start of every list and the work
-//      items of at most kQTile list entries each;
+//      items of at most kAttnTile list entries each;
 //   3. scatter: every (query, kept past block) pair lands at
 //      start(list) + prefix(tile) + rank-in-tile; the position is also kept per
 //      query so the merge can find its partial outputs again.
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void build_lists_kernel(const int32_t* __restr
   for (int64_t e = lo; e < hi; ++e) {
     const int64_t len = totals[e];
     s_len += len;
-    s_items += (len + kQTile - 1) / kQTile;
+    s_items += (len + kAttnTile - 1) / kAttnTile;
   }
   int64_t tot_len, tot_items;
   int64_t pos = block_exclusive_scan(s_len, sh, &tot_len);
@@ -75,18 +75,18 @@ __global__ __launch_bounds__(256) void build_lists_kernel(const int32_t* __restr
   for (int64_t e = lo; e < hi; ++e) {
     const int64_t len = totals[e];
     offs[e] = static_cast<int32_t>(pos);
-    for (int64_t c = 0; c < len; c += kQTile) {
+    for (int64_t c = 0; c < len; c += kAttnTile) {
       WorkItem w;
       w.h = static_cast<int32_t>(e / n);
       w.b = static_cast<int32_t>(e % n);
       w.start = static_cast<int32_t>(pos + c);
-      w.count = static_cast<int32_t>(len - c < kQTile ? len - c : kQTile);
+      w.count = static_cast<int32_t>(len - c < kAttnTile ? len - c : kAttnTile);
       items[it++] = w;
     }
     pos += len;
   }
   if (threadIdx.x == 0) counters[0] = static_cast<int32_t>(tot_items);
-  if (threadIdx.x < kXcds) counters[8 + threadIdx.x] = 0;
+  if (threadIdx.x < kXcds) counters[kCursorStride * (1 + threadIdx.x)] = 0;
 }
 
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ sel, const int32_t* __restrict__ rk,

@@ -17,7 +17,7 @@ struct Problem {
   int ntiles;      // ceil(N / kQTile) gate tiles per head
   int64_t p_off;   // total number of (query, past block) pairs over all heads
   int64_t max_items;   // upper bound on off-diagonal work items
-  int64_t diag_items;  // own-block work items: H * n * ceil(B / kQTile)
+  int64_t diag_items;  // own-block work items: H * n * ceil(B / kAttnTile)
   bool is_f32;
 };
 

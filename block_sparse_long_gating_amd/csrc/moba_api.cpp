@@ -103,8 +103,8 @@ moba::Problem make_problem(int64_t N, int32_t H, int32_t D, int32_t B, int32_t t
   int64_t pairs_per_head = 0;  // sum over blocks j of B * min(topk - 1, j)
   for (int j = 0; j < p.n; ++j) pairs_per_head += static_cast<int64_t>(B) * std::min(topk - 1, j);
   p.p_off = pairs_per_head * H;
-  p.max_items = p.p_off / moba::kQTile + static_cast<int64_t>(H) * p.n;
-  p.diag_items = static_cast<int64_t>(H) * p.n * ((B + moba::kQTile - 1) / moba::kQTile);
+  p.max_items = p.p_off / moba::kAttnTile + static_cast<int64_t>(H) * p.n;
+  p.diag_items = static_cast<int64_t>(H) * p.n * ((B + moba::kAttnTile - 1) / moba::kAttnTile);
   p.is_f32 = is_f32;
   return p;
 }
@@ -142,7 +142,7 @@ WsPlan plan(const moba::Problem& p, bool full) {
     w.qidx = L.add(p.p_off * 4);
     w.inv = L.add(hN * p.lmax * 4);
     w.items = L.add(p.max_items * sizeof(moba::WorkItem));
-    w.counters = L.add(16 * 4);
+    w.counters = L.add(moba::kCounterInts * 4);
     w.part_diag = L.add(hN * p.D * es);
     w.lse_diag = L.add(hN * 4);
     w.part_off = L.add(p.p_off * p.D * es);
