@@ -55,6 +55,8 @@ struct AttnArgs {
   int H, B, n;
   int qt_per_block;     // own-block items per block: ceil(B / kAttnTile)
   int64_t diag_items;   // H * n * qt_per_block
+  int64_t p_off;        // past-block list entries (rows of part_off before the dump rows)
+  int64_t own_items;    // own-block items of the MFMA kernel: H * n * ceil(B / kAttnTile)
   float scale_log2;     // log2(e) / sqrt(D)
 };
 
@@ -105,344 +107,511 @@ __device__ __forceinline__ bool next_item(const int32_t* counters, int32_t* curs
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+constexpr int kWaves = 8;                  // two waves per SIMD, 32 queries each
+constexpr int kThreads = kWaves * kWave;
+constexpr int kSlots = 4;                  // LDS ring slots
+constexpr int kAhead = kSlots - 1;         // loads run this many steps ahead, into the slot of
+                                           // the previous step (all its reads are consumed
+                                           // within that step)
+constexpr int kQTileRows = kAttnTile / 2;  // queries per Q tile (the first or last four waves)
+constexpr int kQBuf = 2 * kAttnTile;       // query-index entries per buffer (one 4-byte load per lane)
+
+// LDS image of one ring slot. A slot holds either one 64-key tile of K and V
+// (row-major, keys on rows) or 128 query rows. Rows are padded so that the
+// 16-byte operand reads of 16 consecutive rows (K, Q) and the 8-byte transpose
+// reads of 4 rows x 32 bytes (V) fall on distinct banks. The slot is filled in
+// 1 KB windows (one 16-byte load per lane); wave w takes windows w, w + 8, ...
 template <int D>
-struct Tile {
-  static constexpr int kChunks = D / 8;                      // 16-byte chunks per key row
-  static constexpr int kRowBytes = D * 2;
-  // Padded LDS row strides. K rows get 16 extra bytes, so the 16 rows one
-  // 16-byte-per-lane operand read touches per LDS cycle hit distinct banks;
-  // V rows get 32, so the 4 rows x 32 bytes of one transpose read do. Plain
-  // padding (not a swizzle) keeps every operand address an immediate offset
-  // from one per-lane base.
-  static constexpr int kKStride = kRowBytes + 16;
-  static constexpr int kVStride = kRowBytes + 32;
-  static constexpr int kKSlotsRow = kKStride / 16;
-  static constexpr int kVSlotsRow = kVStride / 16;
+struct Lay {
+  static constexpr int kKStride = 2 * D + 16;
+  static constexpr int kVStride = 2 * D + (D == 128 ? 48 : 32);
   static constexpr int kKBytes = kKTile * kKStride;
   static constexpr int kVBytes = kKTile * kVStride;
-  // Direct global->LDS loads (16 bytes per lane, 1 KB per wave instruction).
-  // Every wave issues the same number per tile; instructions whose 1 KB
-  // window lies past the end of a tile write into a 1 KB dump area that
-  // follows the tile in the same LDS object.
-  static constexpr int kDump = 1024;
-  static constexpr int kKDma = (kKTile * kKSlotsRow + 511) / 512;
-  static constexpr int kVDma = (kKTile * kVSlotsRow + 511) / 512;
-  static constexpr int kDmaPerTile = kKDma + kVDma;
+  static constexpr int kKSlots16 = kKStride / 16;   // 16-byte units per padded row
+  static constexpr int kVSlots16 = kVStride / 16;
+  static constexpr int kSlot = (kKBytes + kVBytes + 1023) / 1024 * 1024;
+  static constexpr int kWindows = kSlot / 1024;
+  static constexpr int kRoundsHi = (kWindows + kWaves - 1) / kWaves;   // loads per step, waves < kWindows % 8
+  static constexpr int kRoundsLo = kWindows / kWaves;                  // loads per step, the others
+  static constexpr int kChunks = D / 8;             // 16-byte chunks of one row
+  static_assert(kQTileRows * kKStride <= kSlot, "a Q tile must fit one slot");
+  static_assert((kKBytes / 16) % 64 == 0, "K/V boundary must fall on a window");
 };
-
-constexpr int kAttnThreads = 512;
-constexpr int kStages = 4;          // LDS tile buffers; up to kStages - 1 tiles in flight
 
 typedef __attribute__((address_space(3))) void lds_void;
 
 // s_waitcnt immediate for "vmcnt(n)" with the other counters unconstrained (gfx9 encoding).
 constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
-// Per-lane byte offsets (inside one tile of one tensor) of the direct
-// global->LDS loads of this lane: load u fills slot (u * 8 + w) * 64 + lane of
-// the tile's padded LDS image. Windows past the end of the tile re-load row 0
-// and go to the dump area (see dma_tile). Padding slots re-load chunk 0.
-template <int D, int kSlotsRow, int kDma>
-__device__ __forceinline__ void dma_offsets(int64_t row_stride, uint32_t (&off)[kDma]) {
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  constexpr int kSlots = kKTile * kSlotsRow;
-#pragma unroll
-  for (int u = 0; u < kDma; ++u) {
-    const int first = (u * 8 + w) * 64;
-    const int slot = first < kSlots ? first + lane : lane;
-    const int row = slot / kSlotsRow;
-    int c = slot % kSlotsRow;
-    c = c < Tile<D>::kChunks ? c : 0;
-    off[u] = static_cast<uint32_t>((row * row_stride + 8 * c) * 2);
-  }
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  // The low half of the generic address of an LDS object is its offset in the
+  // workgroup's LDS allocation.
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 
-// Issue the direct-to-LDS loads of one tensor tile whose first row is at the
-// (wave-uniform) address `tile` into the LDS stage `lds` (tile image of
-// kSlotsRow * 64 slots followed by the dump area).
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(x)));
+}
+
+__device__ __forceinline__ uint64_t uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  // readfirstlane works on 32-bit ints; each half goes through uint32_t so
+  // that widening never sign-extends.
+  const uint32_t lo = uniform_u32(static_cast<uint32_t>(v));
+  const uint32_t hi = uniform_u32(static_cast<uint32_t>(v >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// The direct global->LDS loads and the partial-output stores are inline asm on
+// purpose: the kernel keeps its own exact count of vector-memory operations in
+// flight (every wave issues the same sequence) and waits on that count, so no
+// memory operation may be hidden from, added to or merged by the compiler's
+// wait-count pass. None of them has a register result, so nothing the compiler
+// allocates can be overwritten by an operation in flight. M0 is written in the
+// same statement as the load that reads it, with the one wait state that an
+// LDS DMA needs after an M0 write.
 //
-// The loads are written as inline asm on purpose. With the compiler builtin,
-// the compiler's wait-count pass cannot tell which ring stage a later LDS read
-// touches and inserts "wait for every outstanding load" before reads, which
-// drains the ring and exposes the full memory latency on most tiles. As asm
-// the loads are invisible to that pass; every wait they need is explicit (see
-// tile_step): each thread waits on the vector-memory counter for its own
-// loads of a tile, then the workgroup barrier publishes the tile. The loads
-// have no register results (they write LDS), so nothing the compiler
-// allocates can be overwritten by a load in flight; M0 is written right before
-// each load inside the same asm statement, with the one wait state a write of
-// M0 needs before an LDS DMA.
-template <int kSlotsRow, int kDma>
-__device__ __forceinline__ void dma_tile(const bf16* tile, const uint32_t* off, char* lds) {
-  const int w = threadIdx.x >> 6;
-  constexpr int kSlots = kKTile * kSlotsRow;
-  // The base is wave-uniform; move it to SGPRs. readfirstlane returns a signed
-  // int: each half goes through uint32_t so that widening never sign-extends.
-  const uint64_t base = reinterpret_cast<uint64_t>(tile);
-  const uint32_t base_lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(base)));
-  const uint32_t base_hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(base >> 32)));
-  const uint64_t sbase = (static_cast<uint64_t>(base_hi) << 32) | static_cast<uint64_t>(base_lo);
-#pragma unroll
-  for (int u = 0; u < kDma; ++u) {
-    const int first = (u * 8 + w) * 64;              // first slot of this wave's 1 KB window
-    char* dst = lds + (first < kSlots ? first * 16 : kSlots * 16);
-    // LDS byte offset of the window: the low half of the generic address of an
-    // LDS object is its offset inside the workgroup's LDS allocation.
-    const uint32_t m0 = static_cast<uint32_t>(
-        __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst)))));
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :
-                 : "s"(m0), "v"(off[u]), "s"(sbase)
-                 : "memory");
-  }
+// They carry no "memory" clobber: the only compiler-visible memory they touch
+// is LDS, and a load always targets a slot no wave reads in the current ring
+// step; every ordering that matters (reads of a slot after the barrier that
+// publishes it, and before the barrier after which it is reloaded) is fixed by
+// the barrier statements, which do clobber memory. Without the clobber the
+// compiler may read the (read-only) work list through scalar loads.
+__device__ __forceinline__ void dma16(uint32_t m0, uint32_t voff, uint64_t sbase) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(uniform_u32(m0)), "v"(voff), "s"(sbase));
 }
 
-// One 64-key tile of work for one wave: S^T = K Q^T, online softmax and
-// O^T += V^T P^T in two halves of 32 keys.
-template <int D>
-__device__ __forceinline__ void tile_compute(const char* ks, const char* vs, const bf16x8 (&qop)[D / 16],
-                                             f32x16 (&o)[D / 32], float& m, float& l, int kt, bool causal,
-                                             int first_pos, int qpos, int half, float c2, bool first_tile) {
-  using T = Tile<D>;
-  constexpr int kDC = D / 32;
-  constexpr int kQC = D / 16;
+__device__ __forceinline__ void dma16_addr(uint32_t m0, const void* addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(uniform_u32(m0)), "v"(addr));
+}
+
+__device__ __forceinline__ void dma4(uint32_t m0, uint32_t voff, uint64_t sbase) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(uniform_u32(m0)), "v"(voff), "s"(sbase));
+}
+
+// Stores read their data registers at issue; the trailing s_nop covers the
+// wait state before those registers may be rewritten.
+__device__ __forceinline__ void store8(void* addr, uint2 data) {
+  asm volatile("global_store_dwordx2 %0, %1, off\n\ts_nop 1" ::"v"(addr), "v"(data));
+}
+
+__device__ __forceinline__ void store4(void* addr, float data) {
+  asm volatile("global_store_dword %0, %1, off\n\ts_nop 1" ::"v"(addr), "v"(data));
+}
+
+// One work item as the kernel sees it. Past-block items: head h, block b, list
+// entries [start, start + count). Own-block items: queries [start, start +
+// count) of block b. nkt: 64-key tiles to visit.
+struct Desc {
+  int h, b, start, count, nkt;
+};
+
+template <bool kCausal>
+__device__ __forceinline__ Desc item_desc(const AttnArgs<bf16>& a, int64_t idx) {
+  Desc d;
+  if (!kCausal) {
+    // Scalar load of the 16-byte descriptor, waited for in the same statement
+    // (the list was written by an earlier kernel and is read-only here).
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    i32x4 v;
+    const uint64_t addr = uniform_ptr(a.items + idx);
+    asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(addr));
+    d.h = v.x;
+    d.b = v.y;
+    d.start = v.z;
+    d.count = v.w;
+    d.nkt = a.B / kKTile;
+  } else {
+    const int per_block = (a.B + kAttnTile - 1) / kAttnTile;
+    const int64_t e = idx / per_block;
+    const int qt = static_cast<int>(idx - e * per_block);
+    d.h = static_cast<int>(e / a.n);
+    d.b = static_cast<int>(e - static_cast<int64_t>(d.h) * a.n);
+    d.start = qt * kAttnTile;
+    d.count = min(kAttnTile, a.B - d.start);
+    d.nkt = (d.start + d.count) / kKTile;
+  }
+  d.h = static_cast<int>(uniform_u32(d.h));
+  d.b = static_cast<int>(uniform_u32(d.b));
+  d.start = static_cast<int>(uniform_u32(d.start));
+  d.count = static_cast<int>(uniform_u32(d.count));
+  d.nkt = static_cast<int>(uniform_u32(d.nkt));
+  return d;
+}
+
+// The 32-query block (item position 32 * blk) of wave i. Own-block items pair
+// the blocks i and 7 - i on the two waves of a SIMD (waves i and i + 4), which
+// evens out the causal triangle across the SIMDs.
+template <bool kCausal>
+__device__ __forceinline__ int wave_block(int i) {
+  return kCausal ? (i < 4 ? i : 11 - i) : i;
+}
+
+// One 32-key half of a K/V tile for the wave's 32 queries.
+//   S^T = K Q^T      keys on rows, queries on columns; K from LDS, Q in registers;
+//   causal mask      on the scores, when the half holds the diagonal;
+//   softmax          p = exp2(s * c2 - m * c2) against the running reference m;
+//                    m is only raised (and O, l rescaled) when this half's
+//                    probabilities sum past 2^kSumLimit, i.e. when a score
+//                    exceeds m by a large margin: rare, decided wave-wide, and
+//                    exact after the final normalisation. l sums the bf16
+//                    probabilities that actually multiply V;
+//   O^T += V^T P^T   V^T read with the LDS transpose read in the key order the
+//                    S accumulator layout hands to P.
+constexpr float kSumLimit = 64.0f;   // log2 of the largest accepted half-tile sum
+
+template <int D, bool kCausal>
+__device__ __forceinline__ void half_tile(const char* kp, const char* vp, const bf16x8 (&q)[D / 16],
+                                          f32x16 (&o)[D / 32], float& m, float& l, bool mask, int kbase, int qpos,
+                                          int half, float c2) {
+  using L = Lay<D>;
+  constexpr int kQC = D / 16, kDC = D / 32;
+  f32x16 s;
 #pragma unroll
-  for (int kh = 0; kh < 2; ++kh) {
-    const int kbase = kt * kKTile + 32 * kh;
-    if (causal && kbase > first_pos + 31) break;   // the whole half is in the future
-    f32x16 s;
+  for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+  for (int c = 0; c < kQC; ++c) {
+    const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kp + 32 * c));
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, q[c], s, 0, 0, 0);
+  }
+  if (kCausal && mask) {
 #pragma unroll
-    for (int c = 0; c < kQC; ++c) {
-      const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ks + 32 * kh * T::kKStride + 32 * c));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[c], s, 0, 0, 0);
+    for (int r = 0; r < 16; ++r)
+      if (kbase + 8 * (r >> 2) + 4 * half + (r & 3) > qpos) s[r] = -INFINITY;
+  }
+  const bf16x2 ones = {static_cast<bf16>(1.f), static_cast<bf16>(1.f)};
+  bf16x8 p[2];
+  float lh = 0.f;
+  {
+    const float mc = m * c2;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const bf16x2 pr = {static_cast<bf16>(__builtin_amdgcn_exp2f(fmaf(s[r], c2, -mc))),
+                         static_cast<bf16>(__builtin_amdgcn_exp2f(fmaf(s[r + 1], c2, -mc)))};
+      p[r >> 3][r & 7] = pr[0];
+      p[r >> 3][(r & 7) + 1] = pr[1];
+      lh = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lh, false);
     }
-    if (causal && kbase + 31 > first_pos) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (kbase + 8 * (r >> 2) + 4 * half + (r & 3) > qpos) s[r] = -INFINITY;
-    }
+  }
+  // Not finite or too large (also the first half of an item, where m = -inf):
+  // raise m to this half's maximum, rescale O and l, recompute p.
+  if (__builtin_amdgcn_ballot_w64(!(lh <= 0x1p64f)) != 0) {
     float mx = fmaxf(s[0], s[1]);
 #pragma unroll
     for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[r], s[r + 1]));
-    mx = wave_max_pair(mx);
-    const float m_new = fmaxf(m, mx);
-    if (first_tile && kh == 0) {
-      m = m_new;                         // O and l are still zero
-    } else if (__builtin_amdgcn_ballot_w64((m_new - m) * c2 > kRescaleThreshold) != 0) {
-      const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c2);
-      m = m_new;
-      l *= alpha;
+    const float m_new = fmaxf(m, fmaxf(mx, __shfl_xor(mx, 32)));
+    const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c2);   // 0 when m was -inf
+    m = m_new;
+    l *= alpha;
 #pragma unroll
-      for (int c = 0; c < kDC; ++c)
+    for (int dc = 0; dc < kDC; ++dc)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[c][r] *= alpha;
-    }
+      for (int r = 0; r < 16; ++r) o[dc][r] *= alpha;
     const float mc = m * c2;
-    bf16x8 p[2];
+    lh = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float e = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -mc));
-      l += e;
-      p[r >> 3][r & 7] = static_cast<bf16>(e);
+    for (int r = 0; r < 16; r += 2) {
+      const bf16x2 pr = {static_cast<bf16>(__builtin_amdgcn_exp2f(fmaf(s[r], c2, -mc))),
+                         static_cast<bf16>(__builtin_amdgcn_exp2f(fmaf(s[r + 1], c2, -mc)))};
+      p[r >> 3][r & 7] = pr[0];
+      p[r >> 3][(r & 7) + 1] = pr[1];
+      lh = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lh, false);
     }
+  }
+  l += lh;
 #pragma unroll
-    for (int dc = 0; dc < kDC; ++dc) {
+  for (int dc = 0; dc < kDC; ++dc) {
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const char* vp = vs + (32 * kh + 16 * g) * T::kVStride + 64 * dc;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * T::kVStride));
-        const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo);
-        const bf16x4 h4 = __builtin_bit_cast(bf16x4, hi);
-        const bf16x8 va = {l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
-        o[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[g], o[dc], 0, 0, 0);
-      }
+    for (int g = 0; g < 2; ++g) {
+      const char* vq = vp + 16 * g * L::kVStride + 64 * dc;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vq));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vq + 8 * L::kVStride));
+      const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo);
+      const bf16x4 h4 = __builtin_bit_cast(bf16x4, hi);
+      const bf16x8 va = {l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
+      o[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[g], o[dc], 0, 0, 0);
     }
   }
 }
 
-// The LDS tile ring. Each stage is a separate __shared__ object so that the
-// compiler can tell a read of one stage from the direct-to-LDS writes still in
-// flight into the others (it would otherwise wait for all of them).
-template <int D> struct Ring {
-  static constexpr int kK = Tile<D>::kKBytes + Tile<D>::kDump, kV = Tile<D>::kVBytes + Tile<D>::kDump;
-};
-#define MOBA_RING(D)                                                  \
-  __shared__ __attribute__((aligned(16))) char k0[Ring<D>::kK];     \
-  __shared__ __attribute__((aligned(16))) char k1[Ring<D>::kK];     \
-  __shared__ __attribute__((aligned(16))) char k2[Ring<D>::kK];     \
-  __shared__ __attribute__((aligned(16))) char k3[Ring<D>::kK];     \
-  __shared__ __attribute__((aligned(16))) char v0[Ring<D>::kV];     \
-  __shared__ __attribute__((aligned(16))) char v1[Ring<D>::kV];     \
-  __shared__ __attribute__((aligned(16))) char v2[Ring<D>::kV];     \
-  __shared__ __attribute__((aligned(16))) char v3[Ring<D>::kV];
-static_assert(kStages == 4, "the ring below has four stages");
-
-struct ItemCtx {
-  const bf16* kblk;
-  const bf16* vblk;
-  int64_t tile_stride;
-  int nkt, last_tile, first_pos, qpos;
-  bool causal, has;
-};
-
-// One pipeline step: tile kt sits in stage (ks, vs); the loads of tile
-// kt + kStages - 1 go to stage (kn, vn), which held tile kt - 1. Every step
-// issues the same loads (a tile past the end re-loads the item's last tile
-// into a stage nobody reads again), so exactly (kStages - 2) * kDmaPerTile
-// loads are younger than tile kt's at the wait below.
-template <int D>
-__device__ __forceinline__ void tile_step(int kt, const ItemCtx& c, const char* ks, const char* vs, char* kn, char* vn,
-                                          const uint32_t (&koff)[Tile<D>::kKDma],
-                                          const uint32_t (&voff)[Tile<D>::kVDma], int k_lane, int v_lane,
-                                          const bf16x8 (&qop)[D / 16], f32x16 (&o)[D / 32], float& m, float& l,
-                                          int half, float c2) {
-  using T = Tile<D>;
-  __builtin_amdgcn_s_waitcnt(wait_vmcnt((kStages - 2) * T::kDmaPerTile));
-  // Tile kt is in LDS for everyone and everyone is done reading tile kt - 1.
-  // A bare barrier (no fence): the only LDS writes here are this thread's
-  // direct loads, already waited for above, and a fence would also wait for
-  // the later tiles still in flight. The memory clobber keeps the compiler
-  // from moving LDS accesses across it.
-  asm volatile("s_barrier" ::: "memory");
-  const int nxt = min(kt + kStages - 1, c.last_tile);
-  dma_tile<T::kKSlotsRow, T::kKDma>(c.kblk + nxt * c.tile_stride, koff, kn);
-  dma_tile<T::kVSlotsRow, T::kVDma>(c.vblk + nxt * c.tile_stride, voff, vn);
-  if (c.has && (!c.causal || kt * kKTile <= c.first_pos + 31))
-    tile_compute<D>(ks + k_lane, vs + v_lane, qop, o, m, l, kt, c.causal, c.first_pos, c.qpos, half, c2, kt == 0);
-}
-
-template <int D>
-__global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs<bf16> a) {
-  using T = Tile<D>;
-  constexpr int kDC = D / 32;   // 32-row blocks of O^T
-  constexpr int kQC = D / 16;   // 16-deep contraction steps of S
-  MOBA_RING(D)
-  __shared__ int s_it;
+// Persistent block-attention kernel over one kind of work item (past-block
+// items from the query lists, or own-block items with the causal mask).
+//
+// Schedule: static. Past-block items: XCD x (= blockIdx % 8) takes a
+// contiguous 1/8 of the item list and its workgroups take every (G/8)-th item
+// of it, so the workgroups of one XCD work on neighbouring items (the same key
+// blocks) at the same time. Own-block items: every workgroup takes a
+// contiguous range, so the query tiles of a block run back to back.
+//
+// Pipeline: each item is a sequence of ring steps: two Q tiles (the item's 256
+// query rows, gathered through the query list into LDS; waves 0-3 take their
+// rows from the first, waves 4-7 from the second), then its 64-key K/V tiles.
+// The loads of step p + kAhead are issued at step p, across item boundaries,
+// into the slot of step p - 1. Every wave issues a fixed number of loads per
+// step (its share of the slot's windows), plus one query-index load at the
+// first step of an item (for the item after it) and the item's stores after
+// its last step, so the number of this wave's memory operations younger than
+// step p's loads is known exactly; step p waits for that count, then a
+// workgroup barrier publishes the slot.
+template <int D, bool kCausal>
+__global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a) {
+  using L = Lay<D>;
+  constexpr int kQC = D / 16, kDC = D / 32;
+  constexpr int kStoresPerItem = kDC * 4 + 1;
+  static_assert((kAhead - 1) * L::kRoundsHi + kStoresPerItem + 1 < 64, "vmcnt holds at most 63");
+  __shared__ __attribute__((aligned(16))) char smem[kSlots * L::kSlot + 2 * kQBuf * 4];
+  char* const ring = smem;
+  int32_t* const qbuf = reinterpret_cast<int32_t*>(smem + kSlots * L::kSlot);
 
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int qn = lane & 31;
   const int half = lane >> 5;
   const float c2 = a.scale_log2;
-  // Per-lane LDS offsets of the operand reads. K operand (row qn, dims
-  // 8*half..): one 16-byte read per 16 dims. V^T operand through the
-  // transpose read: within each 16-lane group, lane (4*e + q) addresses key
-  // row e of the group's 4 keys and dims 4*q..4*q+3 of the group's 16 dims.
-  const int tg = lane >> 4, te = (lane >> 2) & 3, tq = lane & 3;
-  const int k_lane = qn * T::kKStride + 16 * half;
-  const int v_lane = (4 * (tg >> 1) + te) * T::kVStride + 2 * (16 * (tg & 1) + 4 * tq);
-  // Query block of this wave. Waves w and w + 4 share a SIMD; giving them
-  // blocks w and 7 - w evens out the causal triangle of own-block items.
-  const int qblk = w < 4 ? w : 11 - w;
+  const int64_t row_el = static_cast<int64_t>(a.H) * D;        // elements between consecutive tokens
+  const uint32_t row_bytes = static_cast<uint32_t>(row_el * 2);
+  const bool hi_rounds = w < L::kWindows % kWaves || L::kWindows % kWaves == 0;
 
-  const int64_t row_stride = static_cast<int64_t>(a.H) * D;
-  uint32_t koff[T::kKDma], voff[T::kVDma];
-  dma_offsets<D, T::kKSlotsRow, T::kKDma>(row_stride, koff);
-  dma_offsets<D, T::kVSlotsRow, T::kVDma>(row_stride, voff);
+  // ---- static schedule of this workgroup ----
+  int64_t first, stride;
+  int cnt;
+  if (!kCausal) {
+    const int64_t M = a.counters[0];
+    const int xcd = blockIdx.x % kXcds, c = blockIdx.x / kXcds, nper = gridDim.x / kXcds;
+    const int64_t xa = M * xcd / kXcds, xb = M * (xcd + 1) / kXcds;
+    first = xa + c;
+    stride = nper;
+    cnt = first < xb ? static_cast<int>((xb - first + nper - 1) / nper) : 0;
+  } else {
+    const int64_t lo = a.own_items * blockIdx.x / gridDim.x, hi = a.own_items * (blockIdx.x + 1) / gridDim.x;
+    first = lo;
+    stride = 1;
+    cnt = static_cast<int>(hi - lo);
+  }
+  cnt = static_cast<int>(uniform_u32(cnt));
+  if (cnt <= 0) return;
 
-  Item item;
-  while (next_item(a.counters, a.counters + kCursorStride, a.diag_items, a.items, a.n, a.qt_per_block, a.B, &s_it, &item)) {
-    const int h = item.h;
-    ItemCtx c;
-    c.causal = item.causal;
-    c.has = 32 * qblk < item.count;
-    const int slot = 32 * qblk + qn;
-    const int sc = slot < item.count ? slot : item.count - 1;
-    const int64_t qrow = item.causal ? static_cast<int64_t>(item.b) * a.B + item.q0 + sc
-                                     : static_cast<int64_t>(a.qidx[item.list_start + sc]);
-    c.first_pos = item.q0 + 32 * qblk;   // own-block items: position of the block's first query
-    c.qpos = item.q0 + slot;
-    c.nkt = item.causal ? (item.q0 + item.count + kKTile - 1) / kKTile : a.B / kKTile;
-    c.last_tile = c.nkt - 1;
-    c.tile_stride = static_cast<int64_t>(kKTile) * row_stride;
-    c.kblk = a.k + (static_cast<int64_t>(item.b) * a.B * a.H + h) * D;
-    c.vblk = a.v + (static_cast<int64_t>(item.b) * a.B * a.H + h) * D;
-
-    // The first kStages - 1 tiles, then the Q operands, then one full wait:
-    // Q and the first tiles arrive together, and from here on the compiler
-    // sees no load of its own in flight, so it adds no waits inside the tile
-    // loop (the ring loads are managed by the explicit waits in tile_step).
-    dma_tile<T::kKSlotsRow, T::kKDma>(c.kblk, koff, k0);
-    dma_tile<T::kVSlotsRow, T::kVDma>(c.vblk, voff, v0);
-    dma_tile<T::kKSlotsRow, T::kKDma>(c.kblk + min(1, c.last_tile) * c.tile_stride, koff, k1);
-    dma_tile<T::kVSlotsRow, T::kVDma>(c.vblk + min(1, c.last_tile) * c.tile_stride, voff, v1);
-    dma_tile<T::kKSlotsRow, T::kKDma>(c.kblk + min(2, c.last_tile) * c.tile_stride, koff, k2);
-    dma_tile<T::kVSlotsRow, T::kVDma>(c.vblk + min(2, c.last_tile) * c.tile_stride, voff, v2);
-    bf16x8 qop[kQC];
-    {
-      const bf16* qp = a.q + (qrow * a.H + h) * D + 8 * half;
+  // ---- per-lane offsets of the K/V tile loads (tile-relative) ----
+  uint32_t kvoff[L::kRoundsHi];
+  uint32_t vmask = 0;   // bit u: window of round u holds V rows (else K rows or padding)
 #pragma unroll
-      for (int cc = 0; cc < kQC; ++cc) qop[cc] = load_bf16x8(qp + 16 * cc);
+  for (int u = 0; u < L::kRoundsHi; ++u) {
+    const int win = u * kWaves + w;
+    const int s16 = win * 64 + lane;             // 16-byte unit of the slot
+    int row = 0, ch = 0;
+    if (s16 < L::kKBytes / 16) {
+      row = s16 / L::kKSlots16;
+      ch = s16 % L::kKSlots16;
+    } else if (s16 < (L::kKBytes + L::kVBytes) / 16) {
+      const int t = s16 - L::kKBytes / 16;
+      row = t / L::kVSlots16;
+      ch = t % L::kVSlots16;
+      vmask |= 1u << u;
     }
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    ch = ch < L::kChunks ? ch : 0;               // padding units re-load chunk 0
+    kvoff[u] = static_cast<uint32_t>(row) * row_bytes + 16u * ch;
+  }
+  vmask = uniform_u32(vmask);
+  const uint32_t ring_lds = lds_addr(ring);
+  const uint32_t qbuf_lds = lds_addr(qbuf);
 
-    f32x16 o[kDC];
+  // Loads of one ring step (Q tile or K/V tile) of item d into slot `sl`.
+  auto issue_step = [&](const Desc& d, int j, int sl, int qb) {
+    const uint32_t m0base = ring_lds + sl * L::kSlot + w * 1024;
+    if (j >= 2) {
+      const int64_t r0 = static_cast<int64_t>(d.b) * a.B + kKTile * (j - 2);
+      const uint64_t kb = uniform_ptr(a.k + (r0 * a.H + d.h) * D), vb = uniform_ptr(a.v + (r0 * a.H + d.h) * D);
 #pragma unroll
-    for (int cc = 0; cc < kDC; ++cc)
+      for (int u = 0; u < L::kRoundsHi; ++u)
+        if (u < L::kRoundsLo || hi_rounds) dma16(m0base + u * kWaves * 1024, kvoff[u], ((vmask >> u) & 1) ? vb : kb);
+    } else {
+      const int32_t* qi_lds = qbuf + qb * kQBuf;
+      // Opaque copy of the lane index: keeps the per-lane address arithmetic
+      // below from being hoisted out of the loops as long-lived registers.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[cc][r] = 0.f;
-    float m = -INFINITY;   // running maximum of the raw scores (shared by the lane pair of a query)
-    float l = 0.f;         // this lane's share of the softmax denominator
-
-    for (int kt = 0; kt < c.nkt; kt += kStages) {
-      tile_step<D>(kt, c, k0, v0, k3, v3, koff, voff, k_lane, v_lane, qop, o, m, l, half, c2);
-      if (kt + 1 >= c.nkt) break;
-      tile_step<D>(kt + 1, c, k1, v1, k0, v0, koff, voff, k_lane, v_lane, qop, o, m, l, half, c2);
-      if (kt + 2 >= c.nkt) break;
-      tile_step<D>(kt + 2, c, k2, v2, k1, v1, koff, voff, k_lane, v_lane, qop, o, m, l, half, c2);
-      if (kt + 3 >= c.nkt) break;
-      tile_step<D>(kt + 3, c, k3, v3, k2, v2, koff, voff, k_lane, v_lane, qop, o, m, l, half, c2);
+      for (int u = 0; u < L::kRoundsHi; ++u) {
+        if (u < L::kRoundsLo || hi_rounds) {
+          const int s16 = (u * kWaves + w) * 64 + ln;
+          int r = s16 / L::kKSlots16, ch = s16 % L::kKSlots16;
+          r = r < kQTileRows ? r : kQTileRows - 1;
+          ch = ch < L::kChunks ? ch : 0;
+          const int wi = 4 * j + (r >> 5);                      // wave that reads row r
+          const int pos = min(32 * wave_block<kCausal>(wi) + (r & 31), d.count - 1);
+          const int64_t tok = kCausal ? static_cast<int64_t>(d.b) * a.B + d.start + pos
+                                      : static_cast<int64_t>(qi_lds[pos]);
+          dma16_addr(m0base + u * kWaves * 1024, a.q + (tok * a.H + d.h) * D + 8 * ch);
+        }
+      }
     }
+  };
+  // Query-list entries of a past-block item into qbuf[qb] (one 4-byte load per
+  // lane; entries past the item's count repeat its last one).
+  auto issue_qidx = [&](const Desc& d, int qb) {
+    const int i = min(w * 64 + lane, d.count - 1);
+    dma4(qbuf_lds + qb * kQBuf * 4 + w * 256, static_cast<uint32_t>(i) * 4u, uniform_ptr(a.qidx + d.start));
+  };
 
-    // ---- epilogue: normalise, stage the wave's 32 x D output block in LDS
-    // (the ring is free once everyone is past the last tile) and write whole
-    // rows: an item's partial rows are consecutive in memory, so each wave
-    // stores one contiguous run of 32 rows. ----
-    const float l_tot = l + __shfl_xor(l, 32);
-    const float inv_l = 1.f / l_tot;
-    // Retire this thread's loads (the last steps re-load tiles into stages no
-    // one reads; they must not land on the staged output), then wait for all
-    // waves to be done with the ring.
+  // ---- prologue ----
+  Desc dd = item_desc<kCausal>(a, first);     // item being loaded
+  int md = 0, jd = 0;                         // load cursor: item ordinal, step within item
+  bool ddone = false;
+  int qstep0 = -1000, qstep1 = -1000;         // ring step at which each qbuf was requested
+  if (!kCausal) {
+    issue_qidx(dd, 0);
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
     asm volatile("s_barrier" ::: "memory");
-    char* stage = (w < 2 ? k0 : w < 4 ? k1 : w < 6 ? k2 : k3) + (w & 1) * (32 * 2 * D);
-#pragma unroll
-    for (int cc = 0; cc < kDC; ++cc) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        bf16x4 vv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vv[e] = static_cast<bf16>(o[cc][4 * i + e] * inv_l);
-        *reinterpret_cast<uint2*>(stage + (qn * D + 32 * cc + 8 * i + 4 * half) * 2) = __builtin_bit_cast(uint2, vv);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
-    if (c.has) {
-      const int rows = min(32, item.count - 32 * qblk);          // valid rows of this wave's block
-      const int64_t orow0 = item.causal ? static_cast<int64_t>(h) * a.N + static_cast<int64_t>(item.b) * a.B +
-                                              item.q0 + 32 * qblk
-                                        : item.list_start + 32 * qblk;
-      bf16* po = (item.causal ? a.part_diag : a.part_off) + orow0 * D;
-      constexpr int kRowChunks = D / 8;                            // 16-byte chunks per row
-      constexpr int kRowsPerPass = 64 / kRowChunks;
-#pragma unroll
-      for (int r0 = 0; r0 < 32; r0 += kRowsPerPass) {
-        const int r = r0 + lane / kRowChunks;
-        const int ch = lane % kRowChunks;
-        if (r < rows)
-          *reinterpret_cast<uint4*>(po + r * D + 8 * ch) = *reinterpret_cast<const uint4*>(stage + (r * D + 8 * ch) * 2);
-      }
-      if (half == 0 && slot < item.count) {
-        float* pl = (item.causal ? a.lse_diag : a.lse_off) + orow0;
-        pl[qn] = (m * c2 + log2f(l_tot)) * kLn2;
-      }
-    }
   }
+  auto advance_load = [&]() {
+    if (ddone) return;
+    if (++jd == 2 + dd.nkt) {
+      if (md + 1 < cnt) {
+        ++md;
+        jd = 0;
+        dd = item_desc<kCausal>(a, first + static_cast<int64_t>(md) * stride);
+      } else {
+        ddone = true;   // keep re-loading the last K/V tile (into slots nobody reads again)
+        jd = 2 + dd.nkt - 1;
+      }
+    }
+  };
+  // Issue the loads of the load cursor's step into slot sl during ring step `now`.
+  auto load_next = [&](int now, int sl) {
+    if (!kCausal && jd < 2 && !ddone && now < ((md & 1) ? qstep1 : qstep0) + kAhead) {
+      // The query indices of this item may still be in flight: drain and sync.
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+      asm volatile("s_barrier" ::: "memory");
+    }
+    issue_step(dd, jd, sl, md & 1);
+    advance_load();
+  };
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) load_next(0, i);
+
+  // ---- main loop: items, each two Q steps and nkt K/V steps ----
+  const int k_lane = qn * L::kKStride + 16 * half;
+  const int tg = lane >> 4, te = (lane >> 2) & 3, tq = lane & 3;
+  const int v_lane = L::kKBytes + (4 * (tg >> 1) + te) * L::kVStride + 2 * (16 * (tg & 1) + 4 * tq);
+  const int q_lane = (32 * (w & 3) + qn) * L::kKStride + 16 * half;
+  const int pos0 = 32 * wave_block<kCausal>(w);    // this wave's queries: item positions pos0 .. pos0 + 31
+
+  int p = 0;   // ring step
+  // Operations issued after the tile loads of step p - kAhead: query-index
+  // loads at steps p - 1 and p - 2 (one each; at most one of them, items
+  // being at least three steps long), item stores at steps p - 1 .. p - 3.
+  int qh1 = 0, qh2 = 0, sh1 = 0, sh2 = 0, sh3 = 0;
+  // Start ring step p: wait for this wave's loads of the step, publish the slot
+  // to the workgroup, issue the loads of step p + kAhead. Returns the slot of step p.
+  auto ring_step = [&](int qidx_buf, const Desc& nd) -> const char* {
+    const bool xs = (sh1 | sh2 | sh3) != 0;
+    const bool xq = (qh1 | qh2) != 0;
+    constexpr int kHi = (kAhead - 1) * L::kRoundsHi, kLo = (kAhead - 1) * L::kRoundsLo;
+    if (hi_rounds) {
+      if (xs) {
+        if (xq) __builtin_amdgcn_s_waitcnt(wait_vmcnt(kHi + kStoresPerItem + 1));
+        else __builtin_amdgcn_s_waitcnt(wait_vmcnt(kHi + kStoresPerItem));
+      } else {
+        if (xq) __builtin_amdgcn_s_waitcnt(wait_vmcnt(kHi + 1));
+        else __builtin_amdgcn_s_waitcnt(wait_vmcnt(kHi));
+      }
+    } else {
+      if (xs) {
+        if (xq) __builtin_amdgcn_s_waitcnt(wait_vmcnt(kLo + kStoresPerItem + 1));
+        else __builtin_amdgcn_s_waitcnt(wait_vmcnt(kLo + kStoresPerItem));
+      } else {
+        if (xq) __builtin_amdgcn_s_waitcnt(wait_vmcnt(kLo + 1));
+        else __builtin_amdgcn_s_waitcnt(wait_vmcnt(kLo));
+      }
+    }
+    asm volatile("s_barrier" ::: "memory");
+    const bool qnow = !kCausal && qidx_buf >= 0;
+    if (qnow) {
+      issue_qidx(nd, qidx_buf);
+      if (qidx_buf) qstep1 = p;
+      else qstep0 = p;
+    }
+    load_next(p, (p + kAhead) % kSlots);
+    const char* slot = ring + (p % kSlots) * L::kSlot;
+    sh3 = sh2;
+    sh2 = sh1;
+    sh1 = 0;
+    qh2 = qh1;
+    qh1 = qnow ? 1 : 0;
+    ++p;
+    return slot;
+  };
+
+  for (int mc = 0; mc < cnt; ++mc) {
+    const Desc cd = item_desc<kCausal>(a, first + static_cast<int64_t>(mc) * stride);
+    bf16x8 q[kQC];
+    {
+      // The first Q step also requests the query indices of the next item.
+      const bool more = mc + 1 < cnt;
+      Desc nd = cd;
+      if (!kCausal && more) nd = item_desc<kCausal>(a, first + static_cast<int64_t>(mc + 1) * stride);
+      const char* slot = ring_step(more ? (mc + 1) & 1 : -1, nd);
+      if (w < 4) {
+#pragma unroll
+        for (int c = 0; c < kQC; ++c)
+          q[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(slot + q_lane + 32 * c));
+      }
+      slot = ring_step(-1, nd);
+      if (w >= 4) {
+#pragma unroll
+        for (int c = 0; c < kQC; ++c)
+          q[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(slot + q_lane + 32 * c));
+      }
+    }
+    f32x16 o[kDC];
+#pragma unroll
+    for (int dc = 0; dc < kDC; ++dc)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dc][r] = 0.f;
+    float m = -INFINITY, l = 0.f;
+    const bool wave_valid = pos0 < cd.count;
+    const int f = cd.start + pos0;                 // own-block items: block position of the first query
+    const int qpos = f + qn;
+    for (int t = 0; t < cd.nkt; ++t) {
+      const char* slot = ring_step(-1, cd);
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const int kbase = t * kKTile + 32 * kh;
+        if (wave_valid && (!kCausal || kbase <= f))
+          half_tile<D, kCausal>(slot + k_lane + 32 * kh * L::kKStride, slot + v_lane + 32 * kh * L::kVStride, q, o,
+                                m, l, kCausal && kbase == f, kbase, qpos, half, c2);
+      }
+    }
+    // ---- epilogue: normalise and store the item's partial rows ----
+    {
+      const float l_tot = l + __shfl_xor(l, 32);
+      const float inv_l = 1.f / l_tot;
+      const int pos = pos0 + qn;
+      const bool valid = pos < cd.count;
+      int64_t row;
+      if (kCausal)
+        row = valid ? static_cast<int64_t>(cd.h) * a.N + static_cast<int64_t>(cd.b) * a.B + cd.start + pos
+                    : static_cast<int64_t>(a.H) * a.N + pos;
+      else
+        row = valid ? static_cast<int64_t>(cd.start) + pos : a.p_off + pos;
+      bf16* po = (kCausal ? a.part_diag : a.part_off) + row * D + 4 * half;
+#pragma unroll
+      for (int dc = 0; dc < kDC; ++dc)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bf16x4 vv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vv[e] = static_cast<bf16>(o[dc][4 * i + e] * inv_l);
+          store8(po + 32 * dc + 8 * i, __builtin_bit_cast(uint2, vv));
+        }
+      store4((kCausal ? a.lse_diag : a.lse_off) + row, (m * c2 + log2f(l_tot)) * kLn2);
+    }
+    sh1 = 1;
+  }
+  // Retire the trailing (unused) loads before the workgroup's LDS is released.
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
 }
 
 // ------------------------------------------------------------------------------------------
@@ -549,6 +718,8 @@ AttnArgs<T> make_args(const Problem& p, const void* q, const void* k, const void
   a.n = p.n;
   a.qt_per_block = (p.B + kAttnTile - 1) / kAttnTile;
   a.diag_items = p.diag_items;
+  a.p_off = p.p_off;
+  a.own_items = static_cast<int64_t>(p.H) * p.n * ((p.B + kAttnTile - 1) / kAttnTile);
   a.scale_log2 = kLog2e / sqrtf(static_cast<float>(p.D));
   return a;
 }
@@ -557,22 +728,32 @@ AttnArgs<T> make_args(const Problem& p, const void* q, const void* k, const void
 
 hipError_t launch_attention(const Problem& p, const void* q, const void* k, const void* v, const Workspace& ws,
                             int num_cus, hipStream_t stream) {
-  const int64_t total = p.max_items + p.diag_items;
-  int64_t grid = static_cast<int64_t>(num_cus) * (p.is_f32 ? 2 : 1);
-  grid = std::min<int64_t>(grid, ((total + kXcds - 1) / kXcds) * kXcds);
   if (p.is_f32) {
+    const int64_t total = p.max_items + p.diag_items;
+    int64_t grid = static_cast<int64_t>(num_cus) * 2;
+    grid = std::min<int64_t>(grid, ((total + kXcds - 1) / kXcds) * kXcds);
     auto a = make_args<float>(p, q, k, v, ws);
     if (p.D == 128)
       attn_f32_kernel<128><<<static_cast<unsigned>(grid), 256, 0, stream>>>(a);
     else
       attn_f32_kernel<64><<<static_cast<unsigned>(grid), 256, 0, stream>>>(a);
-  } else {
-    auto a = make_args<bf16>(p, q, k, v, ws);
-    if (p.D == 128)
-      attn_bf16_kernel<128><<<static_cast<unsigned>(grid), kAttnThreads, 0, stream>>>(a);
-    else
-      attn_bf16_kernel<64><<<static_cast<unsigned>(grid), kAttnThreads, 0, stream>>>(a);
+    return hipGetLastError();
   }
+  auto a = make_args<bf16>(p, q, k, v, ws);
+  // Past-block items (their number is only known on the device): one
+  // workgroup per CU, a multiple of the XCD count.
+  if (p.lmax > 0) {
+    const int64_t grid = std::max<int64_t>(kXcds, (num_cus / kXcds) * kXcds);
+    if (p.D == 128)
+      attn_mfma_kernel<128, false><<<static_cast<unsigned>(grid), kThreads, 0, stream>>>(a);
+    else
+      attn_mfma_kernel<64, false><<<static_cast<unsigned>(grid), kThreads, 0, stream>>>(a);
+  }
+  const int64_t grid = std::min<int64_t>(num_cus, a.own_items);
+  if (p.D == 128)
+    attn_mfma_kernel<128, true><<<static_cast<unsigned>(grid), kThreads, 0, stream>>>(a);
+  else
+    attn_mfma_kernel<64, true><<<static_cast<unsigned>(grid), kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -17,6 +17,10 @@ constexpr int kWave = 64;
 constexpr int kQTile = 128;
 // Queries per block-attention work item (4 waves x 64 queries).
 constexpr int kAttnTile = 256;
+// Extra partial-output rows past the end of each partial buffer: work-item
+// slots without a query write there, so every lane of the attention kernel
+// stores unconditionally.
+constexpr int kDumpRows = kAttnTile;
 // Keys per attention tile staged in LDS.
 constexpr int kKTile = 64;
 // Number of XCDs (L2 domains) of an MI355X; workgroups are dealt to them round-robin.

@@ -143,10 +143,10 @@ WsPlan plan(const moba::Problem& p, bool full) {
     w.inv = L.add(hN * p.lmax * 4);
     w.items = L.add(p.max_items * sizeof(moba::WorkItem));
     w.counters = L.add(moba::kCounterInts * 4);
-    w.part_diag = L.add(hN * p.D * es);
-    w.lse_diag = L.add(hN * 4);
-    w.part_off = L.add(p.p_off * p.D * es);
-    w.lse_off = L.add(p.p_off * 4);
+    w.part_diag = L.add((hN + moba::kDumpRows) * p.D * es);
+    w.lse_diag = L.add((hN + moba::kDumpRows) * 4);
+    w.part_off = L.add((p.p_off + moba::kDumpRows) * p.D * es);
+    w.lse_off = L.add((p.p_off + moba::kDumpRows) * 4);
     w.sel = L.add(hN * p.topk * 4);
   }
   w.total = L.total;
