@@ -249,80 +249,82 @@ __device__ __forceinline__ int wave_block(int i) {
   return kCausal ? (i < 4 ? i : 11 - i) : i;
 }
 
-// One 32-key half of a K/V tile for the wave's 32 queries.
+// Attention over one 64-key K/V tile for the wave's 32 queries, in 32-key
+// halves.
 //   S^T = K Q^T      keys on rows, queries on columns; K from LDS, Q in registers;
-//   causal mask      on the scores, when the half holds the diagonal;
+//   causal mask      on the scores, when a half holds the diagonal;
 //   softmax          p = exp2(s * c2 - m * c2) against the running reference m;
-//                    m is only raised (and O, l rescaled) when this half's
-//                    probabilities sum past 2^kSumLimit, i.e. when a score
-//                    exceeds m by a large margin: rare, decided wave-wide, and
-//                    exact after the final normalisation. l sums the bf16
-//                    probabilities that actually multiply V;
+//                    m is only raised (and O, l rescaled) when a half's
+//                    probabilities sum past 2^64 or are not finite, i.e. when
+//                    a score exceeds m by a wide margin: rare, decided
+//                    wave-wide, and exact after the final normalisation. l sums
+//                    the bf16 probabilities that actually multiply V;
 //   O^T += V^T P^T   V^T read with the LDS transpose read in the key order the
 //                    S accumulator layout hands to P.
-constexpr float kSumLimit = 64.0f;   // log2 of the largest accepted half-tile sum
+constexpr float kSumLimit = 0x1p64f;   // largest accepted sum of one half's probabilities
 
-template <int D, bool kCausal>
-__device__ __forceinline__ void half_tile(const char* kp, const char* vp, const bf16x8 (&q)[D / 16],
-                                          f32x16 (&o)[D / 32], float& m, float& l, bool mask, int kbase, int qpos,
-                                          int half, float c2) {
-  using L = Lay<D>;
-  constexpr int kQC = D / 16, kDC = D / 32;
+template <int D>
+__device__ __forceinline__ f32x16 scores(const char* kp, const bf16x8 (&q)[D / 16]) {
   f32x16 s;
 #pragma unroll
   for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-  for (int c = 0; c < kQC; ++c) {
+  for (int c = 0; c < D / 16; ++c) {
     const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kp + 32 * c));
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, q[c], s, 0, 0, 0);
   }
-  if (kCausal && mask) {
+  return s;
+}
+
+__device__ __forceinline__ void mask_scores(f32x16& s, int kbase, int qpos, int half) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (kbase + 8 * (r >> 2) + 4 * half + (r & 3) > qpos) s[r] = -INFINITY;
-  }
+  for (int r = 0; r < 16; ++r)
+    if (kbase + 8 * (r >> 2) + 4 * half + (r & 3) > qpos) s[r] = -INFINITY;
+}
+
+// bf16 probabilities of one half against reference mc = m * c2; returns their sum.
+__device__ __forceinline__ float probs(const f32x16& s, float c2, float mc, bf16x8 (&p)[2]) {
   const bf16x2 ones = {static_cast<bf16>(1.f), static_cast<bf16>(1.f)};
-  bf16x8 p[2];
   float lh = 0.f;
-  {
-    const float mc = m * c2;
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const bf16x2 pr = {static_cast<bf16>(__builtin_amdgcn_exp2f(fmaf(s[r], c2, -mc))),
-                         static_cast<bf16>(__builtin_amdgcn_exp2f(fmaf(s[r + 1], c2, -mc)))};
-      p[r >> 3][r & 7] = pr[0];
-      p[r >> 3][(r & 7) + 1] = pr[1];
-      lh = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lh, false);
-    }
+  for (int r = 0; r < 16; r += 2) {
+    const bf16x2 pr = {static_cast<bf16>(__builtin_amdgcn_exp2f(fmaf(s[r], c2, -mc))),
+                       static_cast<bf16>(__builtin_amdgcn_exp2f(fmaf(s[r + 1], c2, -mc)))};
+    p[r >> 3][r & 7] = pr[0];
+    p[r >> 3][(r & 7) + 1] = pr[1];
+    lh = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lh, false);
   }
-  // Not finite or too large (also the first half of an item, where m = -inf):
-  // raise m to this half's maximum, rescale O and l, recompute p.
-  if (__builtin_amdgcn_ballot_w64(!(lh <= 0x1p64f)) != 0) {
-    float mx = fmaxf(s[0], s[1]);
+  return lh;
+}
+
+// The rare path: raise m to the half's maximum (both lanes of a query agree),
+// rescale O and l, recompute the half's probabilities. Taken by the whole wave
+// when any lane's sum is out of range (always on an item's first half, where
+// m = -inf).
+template <int D>
+__device__ __forceinline__ void settle(const f32x16& s, float& m, float& l, f32x16 (&o)[D / 32], bf16x8 (&p)[2],
+                                       float& lh, float c2) {
+  if (__builtin_amdgcn_ballot_w64(!(lh <= kSumLimit)) == 0) return;
+  float mx = fmaxf(s[0], s[1]);
 #pragma unroll
-    for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[r], s[r + 1]));
-    const float m_new = fmaxf(m, fmaxf(mx, __shfl_xor(mx, 32)));
-    const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c2);   // 0 when m was -inf
-    m = m_new;
-    l *= alpha;
+  for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[r], s[r + 1]));
+  const float m_new = fmaxf(m, fmaxf(mx, __shfl_xor(mx, 32)));
+  const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c2);   // 0 when m was -inf
+  m = m_new;
+  l *= alpha;
 #pragma unroll
-    for (int dc = 0; dc < kDC; ++dc)
+  for (int dc = 0; dc < D / 32; ++dc)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[dc][r] *= alpha;
-    const float mc = m * c2;
-    lh = 0.f;
+    for (int r = 0; r < 16; ++r) o[dc][r] *= alpha;
+  lh = probs(s, c2, m * c2, p);
+}
+
+// V^T operands of one half (transpose reads, two per 16-key group and 32 dims).
+template <int D>
+__device__ __forceinline__ void v_operands(const char* vp, bf16x8 (&va)[D / 32][2]) {
+  using L = Lay<D>;
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const bf16x2 pr = {static_cast<bf16>(__builtin_amdgcn_exp2f(fmaf(s[r], c2, -mc))),
-                         static_cast<bf16>(__builtin_amdgcn_exp2f(fmaf(s[r + 1], c2, -mc)))};
-      p[r >> 3][r & 7] = pr[0];
-      p[r >> 3][(r & 7) + 1] = pr[1];
-      lh = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lh, false);
-    }
-  }
-  l += lh;
-#pragma unroll
-  for (int dc = 0; dc < kDC; ++dc) {
+  for (int dc = 0; dc < D / 32; ++dc)
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       const char* vq = vp + 16 * g * L::kVStride + 64 * dc;
@@ -330,10 +332,74 @@ __device__ __forceinline__ void half_tile(const char* kp, const char* vp, const 
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vq + 8 * L::kVStride));
       const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo);
       const bf16x4 h4 = __builtin_bit_cast(bf16x4, hi);
-      const bf16x8 va = {l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
-      o[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[g], o[dc], 0, 0, 0);
+      va[dc][g] = bf16x8{l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
     }
+}
+
+template <int D>
+__device__ __forceinline__ void pv(const bf16x8 (&va)[D / 32][2], const bf16x8 (&p)[2], f32x16 (&o)[D / 32]) {
+#pragma unroll
+  for (int dc = 0; dc < D / 32; ++dc)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) o[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dc][g], p[g], o[dc], 0, 0, 0);
+}
+
+// Scheduling hint for the current region: n groups of (d LDS reads, one
+// MFMA, v VALU instructions), so that the MFMAs of one half are issued in
+// between the VALU work of the other.
+template <int N, int D, int V>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, D, 0);   // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, V, 0);   // VALU
   }
+}
+
+// Both halves of a tile, software-pipelined inside the wave so that the MFMAs
+// of one half run while the VALU work of the other is issued:
+//   S(h0) | S(h1) + softmax(h0) | PV(h0) + softmax(h1) | PV(h1).
+// mask1: the second half holds the diagonal (own-block items).
+template <int D>
+__device__ __forceinline__ void tile_pair(const char* kp, const char* vp, const bf16x8 (&q)[D / 16],
+                                          f32x16 (&o)[D / 32], float& m, float& l, bool mask1, int kbase1, int qpos,
+                                          int half, float c2) {
+  using L = Lay<D>;
+  constexpr int kQC = D / 16;
+  f32x16 s0 = scores<D>(kp, q);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 s1 = scores<D>(kp + 32 * L::kKStride, q);
+  bf16x8 p0[2], va0[D / 32][2];
+  float lh0 = probs(s0, c2, m * c2, p0);
+  v_operands<D>(vp, va0);
+  interleave<kQC, 3, 6>();
+  settle<D>(s0, m, l, o, p0, lh0, c2);
+  l += lh0;
+  if (mask1) mask_scores(s1, kbase1, qpos, half);
+  pv<D>(va0, p0, o);
+  bf16x8 p1[2], va1[D / 32][2];
+  float lh1 = probs(s1, c2, m * c2, p1);
+  v_operands<D>(vp + 32 * L::kVStride, va1);
+  interleave<2 * (D / 32), 2, 6>();
+  settle<D>(s1, m, l, o, p1, lh1, c2);
+  l += lh1;
+  pv<D>(va1, p1, o);
+}
+
+// One half only (own-block items: the tile whose first half holds the diagonal).
+template <int D>
+__device__ __forceinline__ void tile_first_half(const char* kp, const char* vp, const bf16x8 (&q)[D / 16],
+                                                f32x16 (&o)[D / 32], float& m, float& l, int kbase, int qpos,
+                                                int half, float c2) {
+  f32x16 s0 = scores<D>(kp, q);
+  mask_scores(s0, kbase, qpos, half);
+  bf16x8 p0[2], va0[D / 32][2];
+  float lh0 = probs(s0, c2, m * c2, p0);
+  v_operands<D>(vp, va0);
+  settle<D>(s0, m, l, o, p0, lh0, c2);
+  l += lh0;
+  pv<D>(va0, p0, o);
 }
 
 // Persistent block-attention kernel over one kind of work item (past-block
@@ -575,13 +641,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
     const int f = cd.start + pos0;                 // own-block items: block position of the first query
     const int qpos = f + qn;
     for (int t = 0; t < cd.nkt; ++t) {
+      const int kbase = t * kKTile;
       const char* slot = ring_step(-1, cd);
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        const int kbase = t * kKTile + 32 * kh;
-        if (wave_valid && (!kCausal || kbase <= f))
-          half_tile<D, kCausal>(slot + k_lane + 32 * kh * L::kKStride, slot + v_lane + 32 * kh * L::kVStride, q, o,
-                                m, l, kCausal && kbase == f, kbase, qpos, half, c2);
+      if (wave_valid && (!kCausal || kbase < f)) {
+        // Both halves visible (the second may hold the diagonal).
+        tile_pair<D>(slot + k_lane, slot + v_lane, q, o, m, l, kCausal && kbase + 32 == f, kbase + 32, qpos, half,
+                     c2);
+      } else if (kCausal && wave_valid && kbase == f) {
+        tile_first_half<D>(slot + k_lane, slot + v_lane, q, o, m, l, kbase, qpos, half, c2);
       }
     }
     // ---- epilogue: normalise and store the item's partial rows ----
