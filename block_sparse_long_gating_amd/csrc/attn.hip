@@ -45,6 +45,7 @@ struct AttnArgs {
   const T* k;
   const T* v;
   const int32_t* qidx;
+  const int32_t* inv;   // [H][N][lmax] list position of each past-block selection
   const WorkItem* items;
   int32_t* counters;
   T* part_diag;
@@ -57,6 +58,9 @@ struct AttnArgs {
   int64_t diag_items;   // H * n * qt_per_block
   int64_t p_off;        // past-block list entries (rows of part_off before the dump rows)
   int64_t own_items;    // own-block items of the MFMA kernel: H * n * ceil(B / kAttnTile)
+  int topk, lmax;
+  T* out;               // final output [N][H][D] (own-block kernel with the merge fused in)
+  float* lse_out;       // final lse [H][N]
   float scale_log2;     // log2(e) / sqrt(D)
 };
 
@@ -117,6 +121,12 @@ constexpr int kAhead = kSlots - 1;         // loads run this many steps ahead, i
                                            // within that step)
 constexpr int kQTileRows = kAttnTile / 2;  // queries per Q tile (the first or last four waves)
 constexpr int kQBuf = 2 * kAttnTile;       // query-index entries per buffer (one 4-byte load per lane)
+// Own-block items with the merge fused in: list positions of the item's past
+// selections, [query][lmax], loaded into LDS in kInvRounds 4-byte loads per lane.
+constexpr int kFusedMaxPast = 8;
+constexpr int kInvInts = kAttnTile * kFusedMaxPast;
+constexpr int kInvRounds = kInvInts / (kWaves * kWave);
+constexpr int kTailBytes = (2 * kQBuf * 4 > kInvInts * 4) ? 2 * kQBuf * 4 : kInvInts * 4;
 
 // LDS image of one ring slot. A slot holds either one 64-key tile of K and V
 // (row-major, keys on rows) or 128 query rows. Rows are padded so that the
@@ -421,13 +431,21 @@ __device__ __forceinline__ void tile_first_half(const char* kp, const char* vp, 
 // its last step, so the number of this wave's memory operations younger than
 // step p's loads is known exactly; step p waits for that count, then a
 // workgroup barrier publishes the slot.
-template <int D, bool kCausal>
+//
+// kFused (own-block items, at most kFusedMaxPast past selections per query):
+// the item's epilogue also folds in the query's past-block partials (LSE
+// merge) and writes the final out and lse rows.
+template <int D, bool kCausal, bool kFused>
 __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a) {
   using L = Lay<D>;
   constexpr int kQC = D / 16, kDC = D / 32;
   constexpr int kStoresPerItem = kDC * 4 + 1;
-  static_assert((kAhead - 1) * L::kRoundsHi + kStoresPerItem + 1 < 64, "vmcnt holds at most 63");
-  __shared__ __attribute__((aligned(16))) char smem[kSlots * L::kSlot + 2 * kQBuf * 4];
+  // Extra loads at an item's first step: the next item's query indices
+  // (past-block items) or this item's list positions (fused own-block items).
+  constexpr int kXq = kCausal ? (kFused ? kInvRounds : 0) : 1;
+  static_assert(!kFused || kCausal, "the merge is fused into own-block items only");
+  static_assert((kAhead - 1) * L::kRoundsHi + kStoresPerItem + kXq < 64, "vmcnt holds at most 63");
+  __shared__ __attribute__((aligned(16))) char smem[kSlots * L::kSlot + kTailBytes];
   char* const ring = smem;
   int32_t* const qbuf = reinterpret_cast<int32_t*>(smem + kSlots * L::kSlot);
 
@@ -521,6 +539,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
     dma4(qbuf_lds + qb * kQBuf * 4 + w * 256, static_cast<uint32_t>(i) * 4u, uniform_ptr(a.qidx + d.start));
   };
 
+  // List positions of the past selections of an own-block item's queries,
+  // [query][lmax] for its 256 query slots (slots past its count repeat the
+  // last query), into the tail buffer; a fixed kInvRounds loads per lane.
+  auto issue_inv = [&](const Desc& d) {
+    const int64_t row0 = (static_cast<int64_t>(d.h) * a.N + static_cast<int64_t>(d.b) * a.B + d.start) * a.lmax;
+    const int last = max(d.count * a.lmax - 1, 0);
+    // No past selections at all: load (and ignore) the first ints of q instead.
+    const uint64_t src = a.lmax > 0 ? uniform_ptr(a.inv + row0) : uniform_ptr(a.q);
+#pragma unroll
+    for (int u = 0; u < kInvRounds; ++u) {
+      const int e = min((u * kWaves + w) * 64 + lane, last);
+      dma4(qbuf_lds + (u * kWaves + w) * 256, static_cast<uint32_t>(e) * 4u, src);
+    }
+  };
+
   // ---- prologue ----
   Desc dd = item_desc<kCausal>(a, first);     // item being loaded
   int md = 0, jd = 0;                         // load cursor: item ordinal, step within item
@@ -569,6 +602,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
   // loads at steps p - 1 and p - 2 (one each; at most one of them, items
   // being at least three steps long), item stores at steps p - 1 .. p - 3.
   int qh1 = 0, qh2 = 0, sh1 = 0, sh2 = 0, sh3 = 0;
+  int pinv = 0;   // ring step of the current item's first Q step
   // Start ring step p: wait for this wave's loads of the step, publish the slot
   // to the workgroup, issue the loads of step p + kAhead. Returns the slot of step p.
   auto ring_step = [&](int qidx_buf, const Desc& nd) -> const char* {
@@ -577,27 +611,32 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
     constexpr int kHi = (kAhead - 1) * L::kRoundsHi, kLo = (kAhead - 1) * L::kRoundsLo;
     if (hi_rounds) {
       if (xs) {
-        if (xq) __builtin_amdgcn_s_waitcnt(wait_vmcnt(kHi + kStoresPerItem + 1));
+        if (xq) __builtin_amdgcn_s_waitcnt(wait_vmcnt(kHi + kStoresPerItem + kXq));
         else __builtin_amdgcn_s_waitcnt(wait_vmcnt(kHi + kStoresPerItem));
       } else {
-        if (xq) __builtin_amdgcn_s_waitcnt(wait_vmcnt(kHi + 1));
+        if (xq) __builtin_amdgcn_s_waitcnt(wait_vmcnt(kHi + kXq));
         else __builtin_amdgcn_s_waitcnt(wait_vmcnt(kHi));
       }
     } else {
       if (xs) {
-        if (xq) __builtin_amdgcn_s_waitcnt(wait_vmcnt(kLo + kStoresPerItem + 1));
+        if (xq) __builtin_amdgcn_s_waitcnt(wait_vmcnt(kLo + kStoresPerItem + kXq));
         else __builtin_amdgcn_s_waitcnt(wait_vmcnt(kLo + kStoresPerItem));
       } else {
-        if (xq) __builtin_amdgcn_s_waitcnt(wait_vmcnt(kLo + 1));
+        if (xq) __builtin_amdgcn_s_waitcnt(wait_vmcnt(kLo + kXq));
         else __builtin_amdgcn_s_waitcnt(wait_vmcnt(kLo));
       }
     }
     asm volatile("s_barrier" ::: "memory");
-    const bool qnow = !kCausal && qidx_buf >= 0;
+    const bool qnow = kXq > 0 && qidx_buf >= 0;
     if (qnow) {
-      issue_qidx(nd, qidx_buf);
-      if (qidx_buf) qstep1 = p;
-      else qstep0 = p;
+      if (kCausal) {
+        issue_inv(nd);
+        qstep0 = p;
+      } else {
+        issue_qidx(nd, qidx_buf);
+        if (qidx_buf) qstep1 = p;
+        else qstep0 = p;
+      }
     }
     load_next(p, (p + kAhead) % kSlots);
     const char* slot = ring + (p % kSlots) * L::kSlot;
@@ -614,11 +653,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
     const Desc cd = item_desc<kCausal>(a, first + static_cast<int64_t>(mc) * stride);
     bf16x8 q[kQC];
     {
-      // The first Q step also requests the query indices of the next item.
+      // The first Q step also requests the query indices of the next item
+      // (past-block items) or this item's list positions (fused merge).
       const bool more = mc + 1 < cnt;
       Desc nd = cd;
       if (!kCausal && more) nd = item_desc<kCausal>(a, first + static_cast<int64_t>(mc + 1) * stride);
-      const char* slot = ring_step(more ? (mc + 1) & 1 : -1, nd);
+      pinv = p;
+      const char* slot = ring_step(kFused ? 0 : (!kCausal && more ? (mc + 1) & 1 : -1), nd);
       if (w < 4) {
 #pragma unroll
         for (int c = 0; c < kQC; ++c)
@@ -652,7 +693,81 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
       }
     }
     // ---- epilogue: normalise and store the item's partial rows ----
-    {
+    if (kFused) {
+      // LSE merge with the query's past-block partials (natural-log lse_s,
+      // normalised rows O_s): lse = log(exp(lse_own) + sum_s exp(lse_s)),
+      // out = sum over all partials of exp(lse_x - lse) O_x, accumulated in
+      // log2 units with a running maximum.
+      if (p - 1 < pinv + kAhead) {
+        // The list positions may still be in flight (items of under three
+        // steps): drain and sync.
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+        asm volatile("s_barrier" ::: "memory");
+      }
+      const int npast = min(a.topk - 1, cd.b);
+      const int pos = pos0 + qn;
+      const bool valid = pos < cd.count;
+      const int pc = min(pos, cd.count - 1);
+      const float l_tot = l + __shfl_xor(l, 32);
+      float mm = m * c2 + log2f(l_tot);
+      float ww = 1.f;
+      {
+        const float inv_l = 1.f / l_tot;
+#pragma unroll
+        for (int dc = 0; dc < kDC; ++dc)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dc][r] *= inv_l;
+      }
+      const int32_t* ib = qbuf + pc * a.lmax;
+      for (int s0 = 0; s0 < npast; s0 += 2) {
+        const int ns = min(2, npast - s0);
+        uint2 rv[2][kDC][4];
+        float ls[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int ps = ib[s0 + (u < ns ? u : 0)];
+          ls[u] = a.lse_off[ps] * kLog2e;
+          const bf16* rp = a.part_off + static_cast<int64_t>(ps) * D + 4 * half;
+#pragma unroll
+          for (int dc = 0; dc < kDC; ++dc)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rv[u][dc][i] = *reinterpret_cast<const uint2*>(rp + 32 * dc + 8 * i);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          if (u >= ns) break;
+          const float nm = fmaxf(mm, ls[u]);
+          const float ca = __builtin_amdgcn_exp2f(mm - nm), cb = __builtin_amdgcn_exp2f(ls[u] - nm);
+#pragma unroll
+          for (int dc = 0; dc < kDC; ++dc)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const bf16x4 x = __builtin_bit_cast(bf16x4, rv[u][dc][i]);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) o[dc][4 * i + e] = fmaf(o[dc][4 * i + e], ca, static_cast<float>(x[e]) * cb);
+            }
+          ww = fmaf(ww, ca, cb);
+          mm = nm;
+        }
+      }
+      const float inv_w = 1.f / ww;
+      const int64_t tok = static_cast<int64_t>(cd.b) * a.B + cd.start + pos;
+      // Slots without a query write to the dump rows of the own-block buffers.
+      bf16* po = (valid ? a.out + (tok * a.H + cd.h) * D : a.part_diag + (static_cast<int64_t>(a.H) * a.N + pos) * D) +
+                 4 * half;
+#pragma unroll
+      for (int dc = 0; dc < kDC; ++dc)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bf16x4 vv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vv[e] = static_cast<bf16>(o[dc][4 * i + e] * inv_w);
+          store8(po + 32 * dc + 8 * i, __builtin_bit_cast(uint2, vv));
+        }
+      store4(valid ? a.lse_out + static_cast<int64_t>(cd.h) * a.N + tok
+                   : a.lse_diag + static_cast<int64_t>(a.H) * a.N + pos,
+             (mm + log2f(ww)) * kLn2);
+    } else {
       const float l_tot = l + __shfl_xor(l, 32);
       const float inv_l = 1.f / l_tot;
       const int pos = pos0 + qn;
@@ -773,6 +888,7 @@ AttnArgs<T> make_args(const Problem& p, const void* q, const void* k, const void
   a.k = static_cast<const T*>(k);
   a.v = static_cast<const T*>(v);
   a.qidx = ws.qidx;
+  a.inv = ws.inv;
   a.items = ws.items;
   a.counters = ws.counters;
   a.part_diag = static_cast<T*>(ws.part_diag);
@@ -787,14 +903,20 @@ AttnArgs<T> make_args(const Problem& p, const void* q, const void* k, const void
   a.diag_items = p.diag_items;
   a.p_off = p.p_off;
   a.own_items = static_cast<int64_t>(p.H) * p.n * ((p.B + kAttnTile - 1) / kAttnTile);
+  a.topk = p.topk;
+  a.lmax = p.lmax;
+  a.out = nullptr;
+  a.lse_out = nullptr;
   a.scale_log2 = kLog2e / sqrtf(static_cast<float>(p.D));
   return a;
 }
 
 }  // namespace
 
+bool merge_fused(const Problem& p) { return !p.is_f32 && p.lmax <= kFusedMaxPast; }
+
 hipError_t launch_attention(const Problem& p, const void* q, const void* k, const void* v, const Workspace& ws,
-                            int num_cus, hipStream_t stream) {
+                            void* out, float* lse, int num_cus, hipStream_t stream) {
   if (p.is_f32) {
     const int64_t total = p.max_items + p.diag_items;
     int64_t grid = static_cast<int64_t>(num_cus) * 2;
@@ -807,20 +929,32 @@ hipError_t launch_attention(const Problem& p, const void* q, const void* k, cons
     return hipGetLastError();
   }
   auto a = make_args<bf16>(p, q, k, v, ws);
+  a.out = static_cast<bf16*>(out);
+  a.lse_out = lse;
   // Past-block items (their number is only known on the device): one
   // workgroup per CU, a multiple of the XCD count.
   if (p.lmax > 0) {
     const int64_t grid = std::max<int64_t>(kXcds, (num_cus / kXcds) * kXcds);
     if (p.D == 128)
-      attn_mfma_kernel<128, false><<<static_cast<unsigned>(grid), kThreads, 0, stream>>>(a);
+      attn_mfma_kernel<128, false, false><<<static_cast<unsigned>(grid), kThreads, 0, stream>>>(a);
     else
-      attn_mfma_kernel<64, false><<<static_cast<unsigned>(grid), kThreads, 0, stream>>>(a);
+      attn_mfma_kernel<64, false, false><<<static_cast<unsigned>(grid), kThreads, 0, stream>>>(a);
   }
+  // Own-block items after them (same stream), with the merge fused in when
+  // every query keeps at most kFusedMaxPast past blocks.
   const int64_t grid = std::min<int64_t>(num_cus, a.own_items);
-  if (p.D == 128)
-    attn_mfma_kernel<128, true><<<static_cast<unsigned>(grid), kThreads, 0, stream>>>(a);
-  else
-    attn_mfma_kernel<64, true><<<static_cast<unsigned>(grid), kThreads, 0, stream>>>(a);
+  const bool fused = merge_fused(p);
+  if (p.D == 128) {
+    if (fused)
+      attn_mfma_kernel<128, true, true><<<static_cast<unsigned>(grid), kThreads, 0, stream>>>(a);
+    else
+      attn_mfma_kernel<128, true, false><<<static_cast<unsigned>(grid), kThreads, 0, stream>>>(a);
+  } else {
+    if (fused)
+      attn_mfma_kernel<64, true, true><<<static_cast<unsigned>(grid), kThreads, 0, stream>>>(a);
+    else
+      attn_mfma_kernel<64, true, false><<<static_cast<unsigned>(grid), kThreads, 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -33,8 +33,11 @@ hipError_t launch_gate(const Problem& p, const void* q, const Workspace& ws, int
 hipError_t launch_csr(const Problem& p, const Workspace& ws, const int32_t* sel, hipStream_t stream);
 
 // Block attention over the off-diagonal work items and the own-block items.
+// When merge_fused(p), the own-block pass also performs the LSE merge and
+// writes out and lse; launch_merge is then not needed.
+bool merge_fused(const Problem& p);
 hipError_t launch_attention(const Problem& p, const void* q, const void* k, const void* v, const Workspace& ws,
-                            int num_cus, hipStream_t stream);
+                            void* out, float* lse, int num_cus, hipStream_t stream);
 
 // Log-sum-exp merge of the partial outputs into out and lse.
 hipError_t launch_merge(const Problem& p, const Workspace& ws, void* out, float* lse, hipStream_t stream);
