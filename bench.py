@@ -8,8 +8,9 @@ resident in HBM, including the workspace taken from the library's stream-ordered
 pool. Prints one JSON line with the effective TFLOP/s (only the attended,
 causal (query, key) pairs of the selected blocks count, 4*D FLOPs each), the
 fraction of the bf16 MFMA peak, per-stage device times from HIP events the
-library records on its stream, the roofline of the dominant kernel (block
-attention), and the fp64 oracle timed on the host on a sample of query rows.
+library records on its stream, the roofline of the dominant kernel (the
+past-block attention launch), and the fp64 oracle timed on the host on a
+sample of query rows.
 """
 
 from __future__ import annotations
@@ -41,6 +42,13 @@ def effective_pairs(N: int, B: int, topk: int) -> int:
     return sum(B * B * min(topk - 1, j) + B * (B + 1) // 2 for j in range(n))
 
 
+def past_pairs(N: int, B: int, topk: int) -> int:
+    """Attended (query, key) pairs of one head in past (non-own) blocks: the
+    work of the past-block attention kernel."""
+    n = N // B
+    return sum(B * B * min(topk - 1, j) for j in range(n))
+
+
 def row_pairs(rows: np.ndarray, B: int, topk: int) -> int:
     j = rows // B
     return int(np.sum(np.minimum(topk - 1, j) * B + rows % B + 1))
@@ -62,15 +70,16 @@ def device_info():
     return info
 
 
-def traffic_for(ms_attn_per_call: float):
-    """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary, if it was taken with the current kernel source."""
+def traffic_for(workload: str):
+    """HBM bytes per launch of the past-block attention kernel from the
+    committed rocprofv3 counter summary, if it was taken on this workload with
+    the current kernel source (else None)."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
     src_hash = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
-    if t.get("attn_source_sha256") != src_hash:
+    if t.get("attn_source_sha256") != src_hash or t.get("workload") != workload:
         return None
     return t.get("bytes_per_launch")
 
@@ -190,8 +199,11 @@ def main():
     pairs = effective_pairs(w.N, w.block_size, w.topk) * w.H
     flops = 4.0 * w.D * pairs
     tflops = flops / (ms * 1e-3) / 1e12
-    attn_ms = stage_ms["attention"]
-    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    # Dominant kernel: the past-block attention launch; its algorithmic work is
+    # the attended pairs in past blocks, 4 D FLOPs each.
+    past_flops = 4.0 * w.D * past_pairs(w.N, w.block_size, w.topk) * w.H
+    past_ms = stage_ms["attn_past"]
+    past_tflops = past_flops / (past_ms * 1e-3) / 1e12 if past_ms > 0 else 0.0
     info = device_info()
 
     result = {
@@ -214,12 +226,14 @@ def main():
         "stages_us": {s: 1e3 * t for s, t in stage_ms.items()},
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_bf16_kernel (block attention)",
-            "achieved": attn_tflops,
+            "kernel": "attn_mfma_kernel<128, past blocks> (block attention over the query lists)",
+            "achieved": past_tflops,
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": attn_tflops / PEAK_BF16_TFLOPS,
-            "traffic": traffic_for(attn_ms),
+            "frac": past_tflops / PEAK_BF16_TFLOPS,
+            "traffic": traffic_for(w.name),
+            "algorithmic_gflop_per_launch": past_flops / 1e9,
+            "launch_us": 1e3 * past_ms,
         },
         "device": info,
     }

@@ -123,7 +123,7 @@ def gate_topk(q, k, block_size: int, topk: int):
     return sel
 
 
-STAGES = ("pool", "gate", "lists", "attention", "merge")
+STAGES = ("pool", "gate", "lists", "attn_past", "attn_own", "merge")
 STAGE_EVENTS = len(STAGES) + 1
 
 

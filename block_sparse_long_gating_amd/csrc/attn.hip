@@ -916,7 +916,8 @@ AttnArgs<T> make_args(const Problem& p, const void* q, const void* k, const void
 bool merge_fused(const Problem& p) { return !p.is_f32 && p.lmax <= kFusedMaxPast; }
 
 hipError_t launch_attention(const Problem& p, const void* q, const void* k, const void* v, const Workspace& ws,
-                            void* out, float* lse, int num_cus, hipStream_t stream) {
+                            void* out, float* lse, int num_cus, hipStream_t stream,
+                            const std::function<hipError_t(int)>& mark) {
   if (p.is_f32) {
     const int64_t total = p.max_items + p.diag_items;
     int64_t grid = static_cast<int64_t>(num_cus) * 2;
@@ -926,7 +927,8 @@ hipError_t launch_attention(const Problem& p, const void* q, const void* k, cons
       attn_f32_kernel<128><<<static_cast<unsigned>(grid), 256, 0, stream>>>(a);
     else
       attn_f32_kernel<64><<<static_cast<unsigned>(grid), 256, 0, stream>>>(a);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? mark(4) : e;
   }
   auto a = make_args<bf16>(p, q, k, v, ws);
   a.out = static_cast<bf16*>(out);
@@ -940,6 +942,9 @@ hipError_t launch_attention(const Problem& p, const void* q, const void* k, cons
     else
       attn_mfma_kernel<64, false, false><<<static_cast<unsigned>(grid), kThreads, 0, stream>>>(a);
   }
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = mark(4);
+  if (e != hipSuccess) return e;
   // Own-block items after them (same stream), with the merge fused in when
   // every query keeps at most kFusedMaxPast past blocks.
   const int64_t grid = std::min<int64_t>(num_cus, a.own_items);

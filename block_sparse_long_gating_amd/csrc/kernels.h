@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <functional>
+
 #include "common.h"
 
 namespace moba {
@@ -35,9 +37,11 @@ hipError_t launch_csr(const Problem& p, const Workspace& ws, const int32_t* sel,
 // Block attention over the off-diagonal work items and the own-block items.
 // When merge_fused(p), the own-block pass also performs the LSE merge and
 // writes out and lse; launch_merge is then not needed.
+// `mark(4)` is called between the past-block and the own-block launches (stage timing).
 bool merge_fused(const Problem& p);
 hipError_t launch_attention(const Problem& p, const void* q, const void* k, const void* v, const Workspace& ws,
-                            void* out, float* lse, int num_cus, hipStream_t stream);
+                            void* out, float* lse, int num_cus, hipStream_t stream,
+                            const std::function<hipError_t(int)>& mark);
 
 // Log-sum-exp merge of the partial outputs into out and lse.
 hipError_t launch_merge(const Problem& p, const Workspace& ws, void* out, float* lse, hipStream_t stream);

@@ -250,10 +250,10 @@ int prefill_impl(const void* q, const void* k, const void* v, void* out, float* 
   if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess) e = moba::launch_csr(p, ws, ws.sel, stream);
   if (e == hipSuccess) e = mark(3);
-  if (e == hipSuccess) e = moba::launch_attention(p, q, k, v, ws, out, lse, st->num_cus, stream);
-  if (e == hipSuccess) e = mark(4);
-  if (e == hipSuccess && !moba::merge_fused(p)) e = moba::launch_merge(p, ws, out, lse, stream);
+  if (e == hipSuccess) e = moba::launch_attention(p, q, k, v, ws, out, lse, st->num_cus, stream, mark);
   if (e == hipSuccess) e = mark(5);
+  if (e == hipSuccess && !moba::merge_fused(p)) e = moba::launch_merge(p, ws, out, lse, stream);
+  if (e == hipSuccess) e = mark(6);
   return finish(e, base, stream);
 }
 

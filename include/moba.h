@@ -123,10 +123,14 @@ int moba_prefill_fwd_f32(const float* q, const float* k, const float* v, float* 
  * `events` is not NULL, events[0..MOBA_STAGE_EVENTS-1] (created by the caller
  * with hipEventCreate) are recorded on `stream` at the stage boundaries:
  *   0 before the block mean-pool, 1 before the gate/top-k, 2 before the query
- *   lists, 3 before the block attention, 4 before the merge, 5 after it.
+ *   lists, 3 before the past-block attention, 4 before the own-block
+ *   attention (which also performs the LSE merge when every query keeps at
+ *   most 8 past blocks on the bf16 path), 5 before the separate merge (an
+ *   empty stage when it was fused), 6 after it. The fp32 path runs the whole
+ *   block attention in the past-block stage (the own-block stage is empty).
  * hipEventElapsedTime between neighbours gives each stage's device time.
  */
-#define MOBA_STAGE_EVENTS 6
+#define MOBA_STAGE_EVENTS 7
 int moba_prefill_fwd_timed(const void* q, const void* k, const void* v, void* out, float* lse,
                            int64_t N, int32_t H, int32_t D, int32_t block_size, int32_t topk,
                            hipStream_t stream, hipEvent_t* events);
