@@ -7,14 +7,18 @@
 // index; future blocks are never scored (wzjinhao.cn MoBA article, section 3,
 // causal_mask and current_block_force). Rows with j < topk keep all of 0..j.
 //
-// bf16 path: one workgroup = 4 waves x 32 queries. The scores of 32 blocks x
-// 32 queries come from bf16 MFMA (v_mfma_f32_32x32x16_bf16) with the block
-// means as the A operand (rows = blocks) and the queries as the B operand
-// (columns = queries), so each lane ends up holding 16 block scores of one
-// query. The fp32 mean is fed as its exact 3-way bf16 split (hi + mid + lo),
-// and since q is bf16 every product is exact and the score carries only fp32
-// accumulation error. Each lane keeps a sorted register list of the best keys
-// and merges it with the lane 32 away, which holds the other 16 blocks.
+// bf16 path: persistent workgroups of 8 waves x 32 queries, each owning one
+// head and walking pairs of 128-query tiles. The scores of 32 blocks x 32
+// queries come from bf16 MFMA (v_mfma_f32_32x32x16_bf16) with the block means
+// as the A operand (rows = blocks) and the queries as the B operand (columns =
+// queries), so each lane ends up holding 16 block scores of one query. The
+// fp32 mean is fed as its exact 3-way bf16 split (hi + mid + lo), and since q
+// is bf16 every product is exact and the score carries only fp32 accumulation
+// error. The head's split means are staged once in LDS (padded rows, so the
+// 16-byte operand reads of 16 rows hit distinct banks) when they fit, else
+// read from L2; the next tile pair's queries are loaded while the current one
+// is scored. Each lane keeps a sorted register list of the best keys and
+// merges it with the lane 32 away, which holds the other 16 blocks.
 //
 // fp32 path: the same lane layout, but each lane forms full fp32 dot products
 // for every other block with vector FMAs.
@@ -23,6 +27,8 @@
 // which of its 128 queries kept it (an LDS bitmap built with integer ORs), and
 // writes the per-tile count and each query's rank inside the tile. The lists
 // come out ordered by query position, independent of scheduling.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -57,7 +63,7 @@ __device__ __forceinline__ void merge_with_partner(uint64_t (&list)[KCAP]) {
 // list bookkeeping. Called by all 256 threads of the workgroup (it has barriers).
 template <int KCAP>
 __device__ __forceinline__ void finalize(const GateArgs& a, const uint64_t (&list)[KCAP], int64_t t, bool valid,
-                                         int j, uint32_t* bm) {
+                                         int j, uint32_t* bm, int tile) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int qn = lane & 31;
@@ -107,7 +113,6 @@ __device__ __forceinline__ void finalize(const GateArgs& a, const uint64_t (&lis
     }
   }
   __syncthreads();
-  const int tile = blockIdx.x;
   for (int b = threadIdx.x; b < n; b += 256) {
     const int c = __popc(bm[b]) + __popc(bm[n + b]) + __popc(bm[2 * n + b]) + __popc(bm[3 * n + b]);
     a.cnt[(static_cast<int64_t>(h) * n + b) * a.ntiles + tile] = c;
@@ -130,54 +135,95 @@ __device__ __forceinline__ void finalize(const GateArgs& a, const uint64_t (&lis
   }
 }
 
-template <int D, int KCAP>
-__global__ __launch_bounds__(256) void gate_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ pieces,
+// Bytes of one block's row of split means in LDS: 3 pieces of D bf16 plus 16
+// bytes of padding (row stride = 4 banks mod 64).
+template <int D>
+constexpr int gate_lds_row() { return 3 * D * 2 + 16; }
+constexpr int kGateLdsPieces = 64 * 1024;      // largest LDS image of the split means
+constexpr int kGateBitmapDouble = 64 * 1024;   // largest double-buffered bitmap (2 x 4n words)
+
+template <int D, int KCAP, bool kLds>
+__global__ __launch_bounds__(256) void gate_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ pieces,
                                                         GateArgs a) {
-  extern __shared__ uint32_t bm[];
+  extern __shared__ __attribute__((aligned(16))) char gsm[];
+  constexpr int kRow = gate_lds_row<D>();
+  const int n = a.n;
+  const int h = blockIdx.y;
+  char* const plds = gsm;
+  // Query-list bitmaps: two buffers of 4n words when they fit (a buffer is
+  // then rewritten two iterations after it was read), else one buffer and an
+  // extra barrier per iteration.
+  uint32_t* const bmb = reinterpret_cast<uint32_t*>(gsm + (kLds ? n * kRow : 0));
+  const bool two_bm = a.cnt != nullptr && 32 * n <= kGateBitmapDouble;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int qn = lane & 31;
   const int half = lane >> 5;
-  const int h = blockIdx.y;
-  const int64_t t0w = static_cast<int64_t>(blockIdx.x) * kQTile + w * 32;
-  const int64_t t = t0w + qn;
-  const bool valid = t < a.N;
-  const int64_t tc = valid ? t : a.N - 1;
-  const int j = static_cast<int>(tc / a.B);
-  const int64_t tlast = (t0w + 31 < a.N) ? t0w + 31 : a.N - 1;
-  const int jw = static_cast<int>(tlast / a.B);   // largest block of the wave
-
-  uint64_t list[KCAP];
-#pragma unroll
-  for (int s = 0; s < KCAP; ++s) list[s] = 0;
-
-  if (jw >= a.topk && a.topk > 1 && t0w < a.N) {
-    bf16x8 qop[D / 16];
+  const bf16* hp = pieces + static_cast<int64_t>(h) * n * 3 * D;
+  if (kLds) {
+    constexpr int kChunks = 3 * D / 8;   // 16-byte chunks per block row
+    for (int i = threadIdx.x; i < n * kChunks; i += 256) {
+      const int row = i / kChunks, c = i - row * kChunks;
+      *reinterpret_cast<uint4*>(plds + row * kRow + 16 * c) = load_u4(hp + static_cast<int64_t>(row) * 3 * D + 8 * c);
+    }
+    __syncthreads();
+  }
+  auto load_q = [&](int tile, bf16x8 (&op)[D / 16]) {
+    const int64_t t = static_cast<int64_t>(tile) * kQTile + w * 32 + qn;
+    const int64_t tc = t < a.N ? t : a.N - 1;
     const bf16* qrow = q + (tc * a.H + h) * D + 8 * half;
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) qop[c] = load_bf16x8(qrow + 16 * c);
+    for (int c = 0; c < D / 16; ++c) op[c] = load_bf16x8(qrow + 16 * c);
+  };
+  bf16x8 qop[D / 16];
+  load_q(blockIdx.x, qop);
+  int buf = 0;
+  for (int tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+    const int64_t t0w = static_cast<int64_t>(tile) * kQTile + w * 32;
+    const int64_t t = t0w + qn;
+    const bool valid = t < a.N;
+    const int64_t tc = valid ? t : a.N - 1;
+    const int j = static_cast<int>(tc / a.B);
+    const int64_t tlast = (t0w + 31 < a.N) ? t0w + 31 : a.N - 1;
+    const int jw = static_cast<int>(tlast / a.B);   // largest block of the wave
+    // Next tile's queries, in flight while this tile is scored.
+    bf16x8 qnext[D / 16];
+    const int nxt = tile + static_cast<int>(gridDim.x);
+    load_q(nxt < a.ntiles ? nxt : tile, qnext);
 
-    for (int bc = 0; bc * 32 < jw; ++bc) {
-      f32x16 acc;
+    uint64_t list[KCAP];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-      const int brow = min(bc * 32 + qn, a.n - 1);
-      const bf16* prow = pieces + (static_cast<int64_t>(h) * a.n + brow) * 3 * D + 8 * half;
+    for (int s = 0; s < KCAP; ++s) list[s] = 0;
+    if (jw >= a.topk && a.topk > 1 && t0w < a.N) {
+      for (int bc = 0; bc * 32 < jw; ++bc) {
+        f32x16 acc;
 #pragma unroll
-      for (int p = 0; p < 3; ++p) {
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        const int brow = min(bc * 32 + qn, n - 1);
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(load_bf16x8(prow + p * D + 16 * c), qop[c], acc, 0, 0, 0);
+        for (int pc = 0; pc < 3; ++pc) {
+#pragma unroll
+          for (int c = 0; c < D / 16; ++c) {
+            const bf16x8 av = kLds ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                                         plds + brow * kRow + pc * D * 2 + 32 * c + 16 * half))
+                                   : load_bf16x8(hp + static_cast<int64_t>(brow) * 3 * D + pc * D + 16 * c + 8 * half);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qop[c], acc, 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int b = bc * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          topk_insert<KCAP>(list, b < j ? rank_key(acc[r], b) : 0ull);
+        }
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int b = bc * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        topk_insert<KCAP>(list, b < j ? rank_key(acc[r], b) : 0ull);
-      }
+      merge_with_partner<KCAP>(list);
     }
-    merge_with_partner<KCAP>(list);
+    finalize<KCAP>(a, list, t, valid, j, bmb + buf * 4 * n, tile);
+    if (two_bm) buf ^= 1;
+    else if (a.cnt != nullptr) __syncthreads();
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) qop[c] = qnext[c];
   }
-  finalize<KCAP>(a, list, t, valid, j, bm);
 }
 
 template <int D, int KCAP>
@@ -218,11 +264,11 @@ __global__ __launch_bounds__(256) void gate_f32_kernel(const float* __restrict__
     }
     merge_with_partner<KCAP>(list);
   }
-  finalize<KCAP>(a, list, t, valid, j, bm);
+  finalize<KCAP>(a, list, t, valid, j, bm, blockIdx.x);
 }
 
 template <int D, int KCAP>
-hipError_t launch_gate_t(const Problem& p, const void* q, const Workspace& ws, int32_t* sel, bool csr,
+hipError_t launch_gate_t(const Problem& p, const void* q, const Workspace& ws, int32_t* sel, bool csr, int num_cus,
                          hipStream_t stream) {
   GateArgs a;
   a.sel = sel;
@@ -235,32 +281,44 @@ hipError_t launch_gate_t(const Problem& p, const void* q, const Workspace& ws, i
   a.topk = p.topk;
   a.lmax = p.lmax;
   a.ntiles = p.ntiles;
-  dim3 grid(p.ntiles, p.H);
-  const size_t smem = csr ? static_cast<size_t>(4) * p.n * sizeof(uint32_t) : 0;
-  if (p.is_f32)
+  if (p.is_f32) {
+    dim3 grid(p.ntiles, p.H);
+    const size_t smem = csr ? static_cast<size_t>(4) * p.n * sizeof(uint32_t) : 0;
     gate_f32_kernel<D, KCAP><<<grid, 256, smem, stream>>>(static_cast<const float*>(q), ws.kbar, a);
+    return hipGetLastError();
+  }
+  // Persistent: a few workgroups per CU over all heads, each walking every
+  // grid.x-th tile of its head.
+  const int per_head = std::max(1, std::min(p.ntiles, (6 * num_cus + p.H - 1) / p.H));
+  dim3 grid(per_head, p.H);
+  const size_t lds_pieces = static_cast<size_t>(p.n) * gate_lds_row<D>();
+  const size_t bm1 = static_cast<size_t>(4) * p.n * sizeof(uint32_t);
+  const size_t bm = !csr ? 0 : (2 * bm1 <= static_cast<size_t>(kGateBitmapDouble) ? 2 * bm1 : bm1);
+  if (lds_pieces <= kGateLdsPieces)
+    gate_mfma_kernel<D, KCAP, true><<<grid, 256, lds_pieces + bm, stream>>>(static_cast<const bf16*>(q), ws.kpieces, a);
   else
-    gate_bf16_kernel<D, KCAP><<<grid, 256, smem, stream>>>(static_cast<const bf16*>(q), ws.kpieces, a);
+    gate_mfma_kernel<D, KCAP, false><<<grid, 256, bm, stream>>>(static_cast<const bf16*>(q), ws.kpieces, a);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_gate_d(const Problem& p, const void* q, const Workspace& ws, int32_t* sel, bool csr,
+hipError_t launch_gate_d(const Problem& p, const void* q, const Workspace& ws, int32_t* sel, bool csr, int num_cus,
                          hipStream_t stream) {
   const int need = p.topk - 1;  // ranked slots (only used when a row has more past blocks than that)
-  if (need <= 2) return launch_gate_t<D, 2>(p, q, ws, sel, csr, stream);
-  if (need <= 4) return launch_gate_t<D, 4>(p, q, ws, sel, csr, stream);
-  if (need <= 8) return launch_gate_t<D, 8>(p, q, ws, sel, csr, stream);
-  if (need <= 12) return launch_gate_t<D, 12>(p, q, ws, sel, csr, stream);
-  if (need <= 16) return launch_gate_t<D, 16>(p, q, ws, sel, csr, stream);
-  return launch_gate_t<D, 32>(p, q, ws, sel, csr, stream);
+  if (need <= 2) return launch_gate_t<D, 2>(p, q, ws, sel, csr, num_cus, stream);
+  if (need <= 4) return launch_gate_t<D, 4>(p, q, ws, sel, csr, num_cus, stream);
+  if (need <= 8) return launch_gate_t<D, 8>(p, q, ws, sel, csr, num_cus, stream);
+  if (need <= 12) return launch_gate_t<D, 12>(p, q, ws, sel, csr, num_cus, stream);
+  if (need <= 16) return launch_gate_t<D, 16>(p, q, ws, sel, csr, num_cus, stream);
+  return launch_gate_t<D, 32>(p, q, ws, sel, csr, num_cus, stream);
 }
 
 }  // namespace
 
-hipError_t launch_gate(const Problem& p, const void* q, const Workspace& ws, int32_t* sel, bool csr,
+hipError_t launch_gate(const Problem& p, const void* q, const Workspace& ws, int32_t* sel, bool csr, int num_cus,
                        hipStream_t stream) {
-  return p.D == 128 ? launch_gate_d<128>(p, q, ws, sel, csr, stream) : launch_gate_d<64>(p, q, ws, sel, csr, stream);
+  return p.D == 128 ? launch_gate_d<128>(p, q, ws, sel, csr, num_cus, stream)
+                    : launch_gate_d<64>(p, q, ws, sel, csr, num_cus, stream);
 }
 
 }  // namespace moba

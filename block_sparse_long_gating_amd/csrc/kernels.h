@@ -28,7 +28,7 @@ hipError_t launch_pool(const void* k, bool is_f32, float* kbar, bf16* pieces, in
 
 // Gate + causal top-k; writes sel and, when `ws_csr` is true, the per-tile
 // counts and in-tile ranks of the off-diagonal selections.
-hipError_t launch_gate(const Problem& p, const void* q, const Workspace& ws, int32_t* sel, bool ws_csr,
+hipError_t launch_gate(const Problem& p, const void* q, const Workspace& ws, int32_t* sel, bool ws_csr, int num_cus,
                        hipStream_t stream);
 
 // Scans, list scatter and work-list construction.

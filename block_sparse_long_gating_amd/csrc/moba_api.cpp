@@ -222,7 +222,7 @@ int gate_impl(const void* q, const void* k, int32_t* sel, int64_t N, int32_t H, 
   if ((s = alloc_ws(st, w.total, stream, &base)) != MOBA_OK) return s;
   moba::Workspace ws = bind(w, base, false);
   hipError_t e = moba::launch_pool(k, is_f32, ws.kbar, is_f32 ? nullptr : ws.kpieces, N, H, D, B, stream);
-  if (e == hipSuccess) e = moba::launch_gate(p, q, ws, sel, false, stream);
+  if (e == hipSuccess) e = moba::launch_gate(p, q, ws, sel, false, st->num_cus, stream);
   return finish(e, base, stream);
 }
 
@@ -246,7 +246,7 @@ int prefill_impl(const void* q, const void* k, const void* v, void* out, float* 
   hipError_t e = mark(0);
   if (e == hipSuccess) e = moba::launch_pool(k, is_f32, ws.kbar, is_f32 ? nullptr : ws.kpieces, N, H, D, B, stream);
   if (e == hipSuccess) e = mark(1);
-  if (e == hipSuccess) e = moba::launch_gate(p, q, ws, ws.sel, true, stream);
+  if (e == hipSuccess) e = moba::launch_gate(p, q, ws, ws.sel, true, st->num_cus, stream);
   if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess) e = moba::launch_csr(p, ws, ws.sel, stream);
   if (e == hipSuccess) e = mark(3);
