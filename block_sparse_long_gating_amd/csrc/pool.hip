@@ -4,11 +4,12 @@
 // against (wzjinhao.cn MoBA article, section 3, score_pooling = mean; pomoai MoBA
 // overview, "核心原理" step 2). HBM-bound: every key is read exactly once.
 //
-// One workgroup per (block, head). Each thread owns 8 consecutive head-dim
-// lanes of a strided subset of the block's rows (16-byte loads, rows of one
-// token are contiguous), sums them in fp64 in a fixed order, and the per-row
-// group partial sums are combined in LDS in a fixed order, so the result is
-// deterministic and, whenever the fp64 sum is exact, the correctly rounded mean.
+// One workgroup per (block, group of up to 8 heads). Each thread owns 8
+// consecutive dims of one head on a strided subset of the block's rows
+// (16-byte loads; the group's heads of one token are one contiguous run), sums
+// them in fp64 in a fixed order, and the per-row-group partial sums are
+// combined in LDS in a fixed order, so the result is deterministic and,
+// whenever the fp64 sum is exact, the correctly rounded mean.
 // The bf16 path also writes the exact 3-way bf16 split (hi + mid + lo == fp32
 // mean) that the MFMA gate consumes.
 #include "common.h"
@@ -38,38 +39,35 @@ __device__ __forceinline__ void load8<float>(const float* p, float (&x)[8]) {
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void pool_keys_kernel(const T* __restrict__ k, float* __restrict__ kbar,
-                                                        bf16* __restrict__ pieces, int H, int B, int n) {
-  constexpr int kChunks = D / 8;              // threads per token row
-  constexpr int kRowsPerPass = 256 / kChunks; // token rows covered per pass
+                                                        bf16* __restrict__ pieces, int H, int B, int n, int hg) {
   __shared__ double red[256][8];
 
   const int i = blockIdx.x;
-  const int h = blockIdx.y;
-  const int c = threadIdx.x % kChunks;
-  const int r0 = threadIdx.x / kChunks;
+  const int h0 = blockIdx.y * hg;             // this workgroup's heads h0 .. h0 + hg - 1
+  const int chunks = hg * (D / 8);            // threads per token row (16-byte chunks of hg heads)
+  const int rows_per_pass = 256 / chunks;
+  const int c = threadIdx.x % chunks;
+  const int r0 = threadIdx.x / chunks;
   const int64_t row_stride = static_cast<int64_t>(H) * D;
-  const T* base = k + (static_cast<int64_t>(i) * B * H + h) * D + c * 8;
+  // The hg heads of one token are contiguous: each row pass reads hg * 2D bytes in one run.
+  const T* base = k + (static_cast<int64_t>(i) * B * H + h0) * D + c * 8;
 
   double acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0;
 
+  // Eight independent 16-byte loads in flight per thread, added in row order.
   int r = r0;
-  for (; r + 3 * kRowsPerPass < B; r += 4 * kRowsPerPass) {
-    float x0[8], x1[8], x2[8], x3[8];
-    load8<T>(base + static_cast<int64_t>(r) * row_stride, x0);
-    load8<T>(base + static_cast<int64_t>(r + kRowsPerPass) * row_stride, x1);
-    load8<T>(base + static_cast<int64_t>(r + 2 * kRowsPerPass) * row_stride, x2);
-    load8<T>(base + static_cast<int64_t>(r + 3 * kRowsPerPass) * row_stride, x3);
+  for (; r + 7 * rows_per_pass < B; r += 8 * rows_per_pass) {
+    float x[8][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      acc[e] += static_cast<double>(x0[e]);
-      acc[e] += static_cast<double>(x1[e]);
-      acc[e] += static_cast<double>(x2[e]);
-      acc[e] += static_cast<double>(x3[e]);
-    }
+    for (int u = 0; u < 8; ++u) load8<T>(base + static_cast<int64_t>(r + u * rows_per_pass) * row_stride, x[u]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += static_cast<double>(x[u][e]);
   }
-  for (; r < B; r += kRowsPerPass) {
+  for (; r < B; r += rows_per_pass) {
     float x0[8];
     load8<T>(base + static_cast<int64_t>(r) * row_stride, x0);
 #pragma unroll
@@ -80,15 +78,17 @@ __global__ __launch_bounds__(256) void pool_keys_kernel(const T* __restrict__ k,
   for (int e = 0; e < 8; ++e) red[threadIdx.x][e] = acc[e];
   __syncthreads();
 
-  if (threadIdx.x < kChunks) {
+  if (threadIdx.x < chunks) {
     double s[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) s[e] = 0.0;
-    for (int g = 0; g < kRowsPerPass; ++g) {
+    for (int g = 0; g < rows_per_pass; ++g) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s[e] += red[g * kChunks + c][e];
+      for (int e = 0; e < 8; ++e) s[e] += red[g * chunks + c][e];
     }
-    const int64_t o = (static_cast<int64_t>(h) * n + i) * D + c * 8;
+    const int h = h0 + c / (D / 8);
+    const int d0 = (c % (D / 8)) * 8;
+    const int64_t o = (static_cast<int64_t>(h) * n + i) * D + d0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float m = static_cast<float>(s[e] / static_cast<double>(B));
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void pool_keys_kernel(const T* __restrict__ k,
         const bf16 mid = static_cast<bf16>(r1);
         const float r2 = r1 - static_cast<float>(mid);
         const bf16 lo = static_cast<bf16>(r2);
-        const int64_t po = ((static_cast<int64_t>(h) * n + i) * 3) * D + c * 8 + e;
+        const int64_t po = ((static_cast<int64_t>(h) * n + i) * 3) * D + d0 + e;
         pieces[po] = hi;
         pieces[po + D] = mid;
         pieces[po + 2 * D] = lo;
@@ -113,17 +113,22 @@ __global__ __launch_bounds__(256) void pool_keys_kernel(const T* __restrict__ k,
 hipError_t launch_pool(const void* k, bool is_f32, float* kbar, bf16* pieces, int64_t N, int H, int D, int B,
                        hipStream_t stream) {
   const int n = static_cast<int>(N / B);
-  dim3 grid(n, H);
+  // Heads per workgroup: the largest of 8, 4, 2, 1 that divides H (longer
+  // contiguous runs per token row) while leaving at least 1024 workgroups to
+  // keep enough loads in flight, and with a row pass of at most 256 threads.
+  int hg = 8;
+  while (hg > 1 && (H % hg != 0 || hg * (D / 8) > 256 || static_cast<int64_t>(n) * (H / hg) < 1024)) hg /= 2;
+  dim3 grid(n, H / hg);
   if (is_f32) {
     if (D == 128)
-      pool_keys_kernel<float, 128><<<grid, 256, 0, stream>>>(static_cast<const float*>(k), kbar, pieces, H, B, n);
+      pool_keys_kernel<float, 128><<<grid, 256, 0, stream>>>(static_cast<const float*>(k), kbar, pieces, H, B, n, hg);
     else
-      pool_keys_kernel<float, 64><<<grid, 256, 0, stream>>>(static_cast<const float*>(k), kbar, pieces, H, B, n);
+      pool_keys_kernel<float, 64><<<grid, 256, 0, stream>>>(static_cast<const float*>(k), kbar, pieces, H, B, n, hg);
   } else {
     if (D == 128)
-      pool_keys_kernel<bf16, 128><<<grid, 256, 0, stream>>>(static_cast<const bf16*>(k), kbar, pieces, H, B, n);
+      pool_keys_kernel<bf16, 128><<<grid, 256, 0, stream>>>(static_cast<const bf16*>(k), kbar, pieces, H, B, n, hg);
     else
-      pool_keys_kernel<bf16, 64><<<grid, 256, 0, stream>>>(static_cast<const bf16*>(k), kbar, pieces, H, B, n);
+      pool_keys_kernel<bf16, 64><<<grid, 256, 0, stream>>>(static_cast<const bf16*>(k), kbar, pieces, H, B, n, hg);
   }
   return hipGetLastError();
 }
