@@ -141,11 +141,22 @@ struct Lay {
   static constexpr int kVBytes = kKTile * kVStride;
   static constexpr int kKSlots16 = kKStride / 16;   // 16-byte units per padded row
   static constexpr int kVSlots16 = kVStride / 16;
-  static constexpr int kSlot = (kKBytes + kVBytes + 1023) / 1024 * 1024;
-  static constexpr int kWindows = kSlot / 1024;
+  // Windows per slot: a multiple of 8 plus 4, so that exactly waves 0-3 take
+  // one more round than waves 4-7 (the partial steps below rely on it).
+  static constexpr int kWindows = ((kKBytes + kVBytes + 1023) / 1024 + 3) / 8 * 8 + 4;
+  static constexpr int kSlot = kWindows * 1024;
   static constexpr int kRoundsHi = (kWindows + kWaves - 1) / kWaves;   // loads per step, waves < kWindows % 8
   static constexpr int kRoundsLo = kWindows / kWaves;                  // loads per step, the others
   static constexpr int kChunks = D / 8;             // 16-byte chunks of one row
+  // Partial steps (own-block items with the merge fused in): per query of the
+  // item, kPC 32-dim blocks of one past partial row (kSegChunks 16-byte
+  // chunks, swizzled by query), then the partials' log-sum-exps (one float per
+  // query) in the windows of round kRoundsLo, which only waves 0-3 take.
+  static constexpr int kPC = D == 128 ? 2 : 1;
+  static constexpr int kSegChunks = kPC * 4;
+  static constexpr int kLseOff = kAttnTile * kSegChunks * 16;
+  static_assert(kWindows % kWaves == 4, "waves 0-3 take one more round");
+  static_assert(kLseOff == kRoundsLo * kWaves * 1024, "the log-sum-exps fill the last round");
   static_assert(kQTileRows * kKStride <= kSlot, "a Q tile must fit one slot");
   static_assert((kKBytes / 16) % 64 == 0, "K/V boundary must fall on a window");
 };
@@ -213,14 +224,16 @@ __device__ __forceinline__ void store4(void* addr, float data) {
 
 // One work item as the kernel sees it. Past-block items: head h, block b, list
 // entries [start, start + count). Own-block items: queries [start, start +
-// count) of block b. nkt: 64-key tiles to visit.
+// count) of block b. nkt: 64-key tiles to visit; np: partial steps (own-block
+// items with the merge fused in: two per past selection of the block's queries).
 struct Desc {
-  int h, b, start, count, nkt;
+  int h, b, start, count, nkt, np;
 };
 
-template <bool kCausal>
+template <bool kCausal, bool kFused>
 __device__ __forceinline__ Desc item_desc(const AttnArgs<bf16>& a, int64_t idx) {
   Desc d;
+  d.np = 0;
   if (!kCausal) {
     // Scalar load of the 16-byte descriptor, waited for in the same statement
     // (the list was written by an earlier kernel and is read-only here).
@@ -242,12 +255,14 @@ __device__ __forceinline__ Desc item_desc(const AttnArgs<bf16>& a, int64_t idx) 
     d.start = qt * kAttnTile;
     d.count = min(kAttnTile, a.B - d.start);
     d.nkt = (d.start + d.count) / kKTile;
+    if (kFused) d.np = 2 * min(a.topk - 1, d.b);
   }
   d.h = static_cast<int>(uniform_u32(d.h));
   d.b = static_cast<int>(uniform_u32(d.b));
   d.start = static_cast<int>(uniform_u32(d.start));
   d.count = static_cast<int>(uniform_u32(d.count));
   d.nkt = static_cast<int>(uniform_u32(d.nkt));
+  d.np = static_cast<int>(uniform_u32(d.np));
   return d;
 }
 
@@ -371,13 +386,18 @@ __device__ __forceinline__ void interleave() {
 // of one half run while the VALU work of the other is issued:
 //   S(h0) | S(h1) + softmax(h0) | PV(h0) + softmax(h1) | PV(h1).
 // mask1: the second half holds the diagonal (own-block items).
-template <int D>
+// issue(0) and issue(1) put the tile loads of a later ring step in between the
+// phases, so that the address unit works through them while the MFMAs run
+// instead of in one burst at the start of the step.
+template <int D, typename F>
 __device__ __forceinline__ void tile_pair(const char* kp, const char* vp, const bf16x8 (&q)[D / 16],
                                           f32x16 (&o)[D / 32], float& m, float& l, bool mask1, int kbase1, int qpos,
-                                          int half, float c2) {
+                                          int half, float c2, F&& issue) {
   using L = Lay<D>;
   constexpr int kQC = D / 16;
   f32x16 s0 = scores<D>(kp, q);
+  __builtin_amdgcn_sched_barrier(0);
+  issue(0);
   __builtin_amdgcn_sched_barrier(0);
   f32x16 s1 = scores<D>(kp + 32 * L::kKStride, q);
   bf16x8 p0[2], va0[D / 32][2];
@@ -387,6 +407,9 @@ __device__ __forceinline__ void tile_pair(const char* kp, const char* vp, const 
   settle<D>(s0, m, l, o, p0, lh0, c2);
   l += lh0;
   if (mask1) mask_scores(s1, kbase1, qpos, half);
+  __builtin_amdgcn_sched_barrier(0);
+  issue(1);
+  __builtin_amdgcn_sched_barrier(0);
   pv<D>(va0, p0, o);
   bf16x8 p1[2], va1[D / 32][2];
   float lh1 = probs(s1, c2, m * c2, p1);
@@ -433,8 +456,10 @@ __device__ __forceinline__ void tile_first_half(const char* kp, const char* vp, 
 // workgroup barrier publishes the slot.
 //
 // kFused (own-block items, at most kFusedMaxPast past selections per query):
-// the item's epilogue also folds in the query's past-block partials (LSE
-// merge) and writes the final out and lse rows.
+// after its K/V tiles the item takes two more ring steps per past selection,
+// which bring that selection's partial rows (gathered by list position) and
+// their log-sum-exps into a slot; the waves fold them into their rows (LSE
+// merge) and the item ends by writing the final out and lse rows.
 template <int D, bool kCausal, bool kFused>
 __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a) {
   using L = Lay<D>;
@@ -501,15 +526,38 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
   const uint32_t ring_lds = lds_addr(ring);
   const uint32_t qbuf_lds = lds_addr(qbuf);
 
-  // Loads of one ring step (Q tile or K/V tile) of item d into slot `sl`.
-  auto issue_step = [&](const Desc& d, int j, int sl, int qb) {
+  // Loads of one ring step (Q tile, K/V tile or partial step) of item d into slot `sl`.
+  auto issue_step = [&](const Desc& d, int j, int sl, int qb, int u0, int u1) {
     const uint32_t m0base = ring_lds + sl * L::kSlot + w * 1024;
-    if (j >= 2) {
+    if (kFused && j >= 2 + d.nkt) {
+      // Partial step jp: past selection jp / 2, 32-dim blocks kPC * (jp % 2)
+      // onwards, gathered by list position (the item's inv rows in the tail
+      // buffer). Unit (q, c') of the slot takes chunk c' ^ (q % kSegChunks) of
+      // query q's segment; the hi round takes the partials' log-sum-exps.
+      const int jp = j - 2 - d.nkt, sp = jp >> 1;
+      const int dim0 = 32 * L::kPC * (jp & 1);
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+#pragma unroll
+      for (int u = 0; u < L::kRoundsHi; ++u) {
+        if (u >= u0 && u < u1 && u < L::kRoundsLo) {
+          const int s16 = (u * kWaves + w) * 64 + ln;
+          const int q = s16 / L::kSegChunks, cs = s16 % L::kSegChunks;
+          const int ps = qbuf[min(q, d.count - 1) * a.lmax + sp];
+          dma16_addr(m0base + u * kWaves * 1024,
+                     a.part_off + static_cast<int64_t>(ps) * D + dim0 + 8 * (cs ^ (q % L::kSegChunks)));
+        } else if (u >= u0 && u < u1 && u == L::kRoundsLo && hi_rounds) {
+          const int ps = qbuf[min(w * 64 + ln, d.count - 1) * a.lmax + sp];
+          dma4(ring_lds + sl * L::kSlot + L::kLseOff + w * 256, static_cast<uint32_t>(ps) * 4u, uniform_ptr(a.lse_off));
+        }
+      }
+    } else if (j >= 2) {
       const int64_t r0 = static_cast<int64_t>(d.b) * a.B + kKTile * (j - 2);
       const uint64_t kb = uniform_ptr(a.k + (r0 * a.H + d.h) * D), vb = uniform_ptr(a.v + (r0 * a.H + d.h) * D);
 #pragma unroll
       for (int u = 0; u < L::kRoundsHi; ++u)
-        if (u < L::kRoundsLo || hi_rounds) dma16(m0base + u * kWaves * 1024, kvoff[u], ((vmask >> u) & 1) ? vb : kb);
+        if (u >= u0 && u < u1 && (u < L::kRoundsLo || hi_rounds))
+          dma16(m0base + u * kWaves * 1024, kvoff[u], ((vmask >> u) & 1) ? vb : kb);
     } else {
       const int32_t* qi_lds = qbuf + qb * kQBuf;
       // Opaque copy of the lane index: keeps the per-lane address arithmetic
@@ -518,7 +566,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
       asm volatile("" : "+v"(ln));
 #pragma unroll
       for (int u = 0; u < L::kRoundsHi; ++u) {
-        if (u < L::kRoundsLo || hi_rounds) {
+        if (u >= u0 && u < u1 && (u < L::kRoundsLo || hi_rounds)) {
           const int s16 = (u * kWaves + w) * 64 + ln;
           int r = s16 / L::kKSlots16, ch = s16 % L::kKSlots16;
           r = r < kQTileRows ? r : kQTileRows - 1;
@@ -547,15 +595,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
     const int last = max(d.count * a.lmax - 1, 0);
     // No past selections at all: load (and ignore) the first ints of q instead.
     const uint64_t src = a.lmax > 0 ? uniform_ptr(a.inv + row0) : uniform_ptr(a.q);
+    int ln = lane;   // opaque copy: the offsets below are not kept live across the item
+    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int u = 0; u < kInvRounds; ++u) {
-      const int e = min((u * kWaves + w) * 64 + lane, last);
+      const int e = min((u * kWaves + w) * 64 + ln, last);
       dma4(qbuf_lds + (u * kWaves + w) * 256, static_cast<uint32_t>(e) * 4u, src);
     }
   };
 
   // ---- prologue ----
-  Desc dd = item_desc<kCausal>(a, first);     // item being loaded
+  Desc dd = item_desc<kCausal, kFused>(a, first);     // item being loaded
   int md = 0, jd = 0;                         // load cursor: item ordinal, step within item
   bool ddone = false;
   int qstep0 = -1000, qstep1 = -1000;         // ring step at which each qbuf was requested
@@ -566,27 +616,35 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
   }
   auto advance_load = [&]() {
     if (ddone) return;
-    if (++jd == 2 + dd.nkt) {
+    if (++jd == 2 + dd.nkt + dd.np) {
       if (md + 1 < cnt) {
         ++md;
         jd = 0;
-        dd = item_desc<kCausal>(a, first + static_cast<int64_t>(md) * stride);
+        dd = item_desc<kCausal, kFused>(a, first + static_cast<int64_t>(md) * stride);
       } else {
         ddone = true;   // keep re-loading the last K/V tile (into slots nobody reads again)
         jd = 2 + dd.nkt - 1;
       }
     }
   };
-  // Issue the loads of the load cursor's step into slot sl during ring step `now`.
-  auto load_next = [&](int now, int sl) {
-    if (!kCausal && jd < 2 && !ddone && now < ((md & 1) ? qstep1 : qstep0) + kAhead) {
+  // Issue the loads of the load cursor's step into slot sl during ring step
+  // `now`: rounds [u0, u1) of it; the part that ends with the last round also
+  // moves the cursor on.
+  auto load_part = [&](int now, int sl, int u0, int u1) {
+    if (u0 == 0 && !kCausal && jd < 2 && !ddone && now < ((md & 1) ? qstep1 : qstep0) + kAhead) {
       // The query indices of this item may still be in flight: drain and sync.
       __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
       asm volatile("s_barrier" ::: "memory");
     }
-    issue_step(dd, jd, sl, md & 1);
-    advance_load();
+    if (u0 == 0 && kFused && jd >= 2 + dd.nkt && !ddone && now < qstep0 + kAhead) {
+      // The list positions of this item may still be in flight: drain and sync.
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+      asm volatile("s_barrier" ::: "memory");
+    }
+    issue_step(dd, jd, sl, md & 1, u0, u1);
+    if (u1 == L::kRoundsHi) advance_load();
   };
+  auto load_next = [&](int now, int sl) { load_part(now, sl, 0, L::kRoundsHi); };
 #pragma unroll
   for (int i = 0; i < kAhead; ++i) load_next(0, i);
 
@@ -602,10 +660,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
   // loads at steps p - 1 and p - 2 (one each; at most one of them, items
   // being at least three steps long), item stores at steps p - 1 .. p - 3.
   int qh1 = 0, qh2 = 0, sh1 = 0, sh2 = 0, sh3 = 0;
-  int pinv = 0;   // ring step of the current item's first Q step
   // Start ring step p: wait for this wave's loads of the step, publish the slot
   // to the workgroup, issue the loads of step p + kAhead. Returns the slot of step p.
-  auto ring_step = [&](int qidx_buf, const Desc& nd) -> const char* {
+  // With `defer`, the loads of step p + kAhead are left to the caller (split
+  // into two parts by the tile computation).
+  auto ring_step = [&](int qidx_buf, const Desc& nd, bool defer) -> const char* {
     const bool xs = (sh1 | sh2 | sh3) != 0;
     const bool xq = (qh1 | qh2) != 0;
     constexpr int kHi = (kAhead - 1) * L::kRoundsHi, kLo = (kAhead - 1) * L::kRoundsLo;
@@ -638,7 +697,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
         else qstep0 = p;
       }
     }
-    load_next(p, (p + kAhead) % kSlots);
+    if (!defer) load_next(p, (p + kAhead) % kSlots);
     const char* slot = ring + (p % kSlots) * L::kSlot;
     sh3 = sh2;
     sh2 = sh1;
@@ -650,22 +709,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
   };
 
   for (int mc = 0; mc < cnt; ++mc) {
-    const Desc cd = item_desc<kCausal>(a, first + static_cast<int64_t>(mc) * stride);
+    const Desc cd = item_desc<kCausal, kFused>(a, first + static_cast<int64_t>(mc) * stride);
     bf16x8 q[kQC];
     {
       // The first Q step also requests the query indices of the next item
       // (past-block items) or this item's list positions (fused merge).
       const bool more = mc + 1 < cnt;
       Desc nd = cd;
-      if (!kCausal && more) nd = item_desc<kCausal>(a, first + static_cast<int64_t>(mc + 1) * stride);
-      pinv = p;
-      const char* slot = ring_step(kFused ? 0 : (!kCausal && more ? (mc + 1) & 1 : -1), nd);
+      if (!kCausal && more) nd = item_desc<kCausal, kFused>(a, first + static_cast<int64_t>(mc + 1) * stride);
+      const char* slot = ring_step(kFused ? 0 : (!kCausal && more ? (mc + 1) & 1 : -1), nd, false);
       if (w < 4) {
 #pragma unroll
         for (int c = 0; c < kQC; ++c)
           q[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(slot + q_lane + 32 * c));
       }
-      slot = ring_step(-1, nd);
+      slot = ring_step(-1, nd, false);
       if (w >= 4) {
 #pragma unroll
         for (int c = 0; c < kQC; ++c)
@@ -683,13 +741,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
     const int qpos = f + qn;
     for (int t = 0; t < cd.nkt; ++t) {
       const int kbase = t * kKTile;
-      const char* slot = ring_step(-1, cd);
+      const char* slot = ring_step(-1, cd, true);
+      const int now = p - 1, sl = (now + kAhead) % kSlots;
+      constexpr int kSplit = (L::kRoundsHi + 1) / 2;
+      auto issue = [&](int part) {
+        if (part == 0) load_part(now, sl, 0, kSplit);
+        else load_part(now, sl, kSplit, L::kRoundsHi);
+      };
       if (wave_valid && (!kCausal || kbase < f)) {
         // Both halves visible (the second may hold the diagonal).
         tile_pair<D>(slot + k_lane, slot + v_lane, q, o, m, l, kCausal && kbase + 32 == f, kbase + 32, qpos, half,
-                     c2);
-      } else if (kCausal && wave_valid && kbase == f) {
-        tile_first_half<D>(slot + k_lane, slot + v_lane, q, o, m, l, kbase, qpos, half, c2);
+                     c2, issue);
+      } else {
+        load_next(now, sl);
+        if (kCausal && wave_valid && kbase == f)
+          tile_first_half<D>(slot + k_lane, slot + v_lane, q, o, m, l, kbase, qpos, half, c2);
       }
     }
     // ---- epilogue: normalise and store the item's partial rows ----
@@ -697,17 +763,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
       // LSE merge with the query's past-block partials (natural-log lse_s,
       // normalised rows O_s): lse = log(exp(lse_own) + sum_s exp(lse_s)),
       // out = sum over all partials of exp(lse_x - lse) O_x, accumulated in
-      // log2 units with a running maximum.
-      if (p - 1 < pinv + kAhead) {
-        // The list positions may still be in flight (items of under three
-        // steps): drain and sync.
-        __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
-        asm volatile("s_barrier" ::: "memory");
-      }
-      const int npast = min(a.topk - 1, cd.b);
+      // log2 units with a running maximum. The partial rows come through the
+      // ring in the item's partial steps, two per past selection (kPC 32-dim
+      // blocks each); the first of the two also carries their log-sum-exps.
       const int pos = pos0 + qn;
       const bool valid = pos < cd.count;
-      const int pc = min(pos, cd.count - 1);
       const float l_tot = l + __shfl_xor(l, 32);
       float mm = m * c2 + log2f(l_tot);
       float ww = 1.f;
@@ -718,36 +778,38 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[dc][r] *= inv_l;
       }
-      const int32_t* ib = qbuf + pc * a.lmax;
-      for (int s0 = 0; s0 < npast; s0 += 2) {
-        const int ns = min(2, npast - s0);
-        uint2 rv[2][kDC][4];
-        float ls[2];
+      for (int sp = 0; sp < cd.np / 2; ++sp) {
+        // This lane's bytes of its query's segment and the query's swizzle,
+        // from an opaque copy of the lane index (nothing of the merge is kept
+        // live across the item's tiles).
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int lpos = pos0 + (ln & 31);
+        const int seg = lpos * L::kSegChunks * 16 + 8 * (ln >> 5);
+        const int sw = lpos % L::kSegChunks;
+        float ca = 1.f, cb = 0.f;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int ps = ib[s0 + (u < ns ? u : 0)];
-          ls[u] = a.lse_off[ps] * kLog2e;
-          const bf16* rp = a.part_off + static_cast<int64_t>(ps) * D + 4 * half;
+        for (int pc = 0; pc < 2; ++pc) {
+          const char* slot = ring_step(-1, cd, false);
+          if (pc == 0) {
+            const float ls = *reinterpret_cast<const float*>(slot + L::kLseOff + 4 * lpos) * kLog2e;
+            const float nm = fmaxf(mm, ls);
+            ca = __builtin_amdgcn_exp2f(mm - nm);
+            cb = __builtin_amdgcn_exp2f(ls - nm);
+            ww = fmaf(ww, ca, cb);
+            mm = nm;
+          }
 #pragma unroll
-          for (int dc = 0; dc < kDC; ++dc)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) rv[u][dc][i] = *reinterpret_cast<const uint2*>(rp + 32 * dc + 8 * i);
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          if (u >= ns) break;
-          const float nm = fmaxf(mm, ls[u]);
-          const float ca = __builtin_amdgcn_exp2f(mm - nm), cb = __builtin_amdgcn_exp2f(ls[u] - nm);
-#pragma unroll
-          for (int dc = 0; dc < kDC; ++dc)
+          for (int dl = 0; dl < L::kPC; ++dl)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const bf16x4 x = __builtin_bit_cast(bf16x4, rv[u][dc][i]);
+              const bf16x4 x = __builtin_bit_cast(
+                  bf16x4, *reinterpret_cast<const uint2*>(slot + seg + 16 * ((4 * dl + i) ^ sw)));
 #pragma unroll
-              for (int e = 0; e < 4; ++e) o[dc][4 * i + e] = fmaf(o[dc][4 * i + e], ca, static_cast<float>(x[e]) * cb);
+              for (int e = 0; e < 4; ++e)
+                o[L::kPC * pc + dl][4 * i + e] =
+                    fmaf(o[L::kPC * pc + dl][4 * i + e], ca, static_cast<float>(x[e]) * cb);
             }
-          ww = fmaf(ww, ca, cb);
-          mm = nm;
         }
       }
       const float inv_w = 1.f / ww;
