@@ -115,10 +115,14 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;                  // two waves per SIMD, 32 queries each
 constexpr int kThreads = kWaves * kWave;
-constexpr int kSlots = 4;                  // LDS ring slots
+constexpr int kSlots = 3;                  // LDS ring slots
 constexpr int kAhead = kSlots - 1;         // loads run this many steps ahead, into the slot of
                                            // the previous step (all its reads are consumed
                                            // within that step)
+static_assert(kAhead == 2, "the wait counts below track the two previous steps");
+// Per-wave staging of the item's output rows: 32 rows of 64 dims (128 bytes,
+// 16-byte chunks swizzled by row), so that the rows leave in full 128-byte lines.
+constexpr int kStageBytes = 32 * 128;
 constexpr int kQTileRows = kAttnTile / 2;  // queries per Q tile (the first or last four waves)
 constexpr int kQBuf = 2 * kAttnTile;       // query-index entries per buffer (one 4-byte load per lane)
 // Own-block items with the merge fused in: list positions of the item's past
@@ -212,10 +216,13 @@ __device__ __forceinline__ void dma4(uint32_t m0, uint32_t voff, uint64_t sbase)
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(uniform_u32(m0)), "v"(voff), "s"(sbase));
 }
 
+typedef int i32x4v __attribute__((ext_vector_type(4)));
+
 // Stores read their data registers at issue; the trailing s_nop covers the
 // wait state before those registers may be rewritten.
-__device__ __forceinline__ void store8(void* addr, uint2 data) {
-  asm volatile("global_store_dwordx2 %0, %1, off\n\ts_nop 1" ::"v"(addr), "v"(data));
+__device__ __forceinline__ void store16(void* addr, uint4 d) {
+  const i32x4v data = {static_cast<int>(d.x), static_cast<int>(d.y), static_cast<int>(d.z), static_cast<int>(d.w)};
+  asm volatile("global_store_dwordx4 %0, %1, off\n\ts_nop 1" ::"v"(addr), "v"(data));
 }
 
 __device__ __forceinline__ void store4(void* addr, float data) {
@@ -464,15 +471,17 @@ template <int D, bool kCausal, bool kFused>
 __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a) {
   using L = Lay<D>;
   constexpr int kQC = D / 16, kDC = D / 32;
-  constexpr int kStoresPerItem = kDC * 4 + 1;
+  // Item stores: four 16-byte stores per 64-dim round, and the log-sum-exps.
+  constexpr int kStoresPerItem = 4 * (kDC / 2) + 1;
   // Extra loads at an item's first step: the next item's query indices
   // (past-block items) or this item's list positions (fused own-block items).
   constexpr int kXq = kCausal ? (kFused ? kInvRounds : 0) : 1;
   static_assert(!kFused || kCausal, "the merge is fused into own-block items only");
   static_assert((kAhead - 1) * L::kRoundsHi + kStoresPerItem + kXq < 64, "vmcnt holds at most 63");
-  __shared__ __attribute__((aligned(16))) char smem[kSlots * L::kSlot + kTailBytes];
+  __shared__ __attribute__((aligned(16))) char smem[kSlots * L::kSlot + kWaves * kStageBytes + kTailBytes];
   char* const ring = smem;
-  int32_t* const qbuf = reinterpret_cast<int32_t*>(smem + kSlots * L::kSlot);
+  char* const stage = smem + kSlots * L::kSlot;
+  int32_t* const qbuf = reinterpret_cast<int32_t*>(smem + kSlots * L::kSlot + kWaves * kStageBytes);
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -656,17 +665,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
   const int pos0 = 32 * wave_block<kCausal>(w);    // this wave's queries: item positions pos0 .. pos0 + 31
 
   int p = 0;   // ring step
-  // Operations issued after the tile loads of step p - kAhead: query-index
-  // loads at steps p - 1 and p - 2 (one each; at most one of them, items
-  // being at least three steps long), item stores at steps p - 1 .. p - 3.
-  int qh1 = 0, qh2 = 0, sh1 = 0, sh2 = 0, sh3 = 0;
+  // Operations issued after the tile loads of step p - kAhead (= p - 2):
+  // query-index or list-position loads at step p - 1 (they precede the step's
+  // tile loads), item stores at steps p - 1 and p - 2 (they follow them; at
+  // most one item's, items being at least three steps long).
+  int qh1 = 0, sh1 = 0, sh2 = 0;
   // Start ring step p: wait for this wave's loads of the step, publish the slot
   // to the workgroup, issue the loads of step p + kAhead. Returns the slot of step p.
   // With `defer`, the loads of step p + kAhead are left to the caller (split
   // into two parts by the tile computation).
   auto ring_step = [&](int qidx_buf, const Desc& nd, bool defer) -> const char* {
-    const bool xs = (sh1 | sh2 | sh3) != 0;
-    const bool xq = (qh1 | qh2) != 0;
+    const bool xs = (sh1 | sh2) != 0;
+    const bool xq = qh1 != 0;
     constexpr int kHi = (kAhead - 1) * L::kRoundsHi, kLo = (kAhead - 1) * L::kRoundsLo;
     if (hi_rounds) {
       if (xs) {
@@ -685,6 +695,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
         else __builtin_amdgcn_s_waitcnt(wait_vmcnt(kLo));
       }
     }
+    // This wave's reads of earlier slots have returned before the barrier
+    // after which other waves may reload them.
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
     const bool qnow = kXq > 0 && qidx_buf >= 0;
     if (qnow) {
@@ -699,13 +712,46 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
     }
     if (!defer) load_next(p, (p + kAhead) % kSlots);
     const char* slot = ring + (p % kSlots) * L::kSlot;
-    sh3 = sh2;
     sh2 = sh1;
     sh1 = 0;
-    qh2 = qh1;
     qh1 = qnow ? 1 : 0;
     ++p;
     return slot;
+  };
+
+  // Writes the wave's 32 output rows (item positions pos0 .. pos0 + 31, each
+  // query's values times `scale`) through the wave's staging area, one 64-dim
+  // round at a time: lane (qn, half) puts its values into 16-byte chunks
+  // swizzled by row, then 8 lanes per row read them back and store 128-byte
+  // lines. rowp(pos): first element of the output row of item position pos.
+  // The wave's LDS operations run in order, so the staging area needs no barrier.
+  auto store_tile = [&](const f32x16 (&ov)[kDC], float scale, auto&& rowp) {
+    char* const st = stage + w * kStageBytes;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int wr = ln & 31, wh = ln >> 5;   // writer: row, half
+    const int rr = ln >> 3, rc = ln & 7;    // reader: row within a group of 8, chunk
+#pragma unroll
+    for (int rd = 0; rd < kDC / 2; ++rd) {
+#pragma unroll
+      for (int dl = 0; dl < 2; ++dl)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bf16x4 vv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vv[e] = static_cast<bf16>(ov[2 * rd + dl][4 * i + e] * scale);
+          const int c = 4 * dl + i;
+          *reinterpret_cast<uint2*>(st + wr * 128 + 16 * (c ^ (wr & 7)) + 8 * wh) = __builtin_bit_cast(uint2, vv);
+        }
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int r = 8 * k + rr;
+        const uint4 x = *reinterpret_cast<const uint4*>(st + r * 128 + 16 * (rc ^ rr));
+        store16(rowp(pos0 + r) + 64 * rd + 8 * rc, x);
+      }
+      asm volatile("" ::: "memory");
+    }
   };
 
   for (int mc = 0; mc < cnt; ++mc) {
@@ -812,20 +858,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
             }
         }
       }
-      const float inv_w = 1.f / ww;
       const int64_t tok = static_cast<int64_t>(cd.b) * a.B + cd.start + pos;
       // Slots without a query write to the dump rows of the own-block buffers.
-      bf16* po = (valid ? a.out + (tok * a.H + cd.h) * D : a.part_diag + (static_cast<int64_t>(a.H) * a.N + pos) * D) +
-                 4 * half;
-#pragma unroll
-      for (int dc = 0; dc < kDC; ++dc)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          bf16x4 vv;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) vv[e] = static_cast<bf16>(o[dc][4 * i + e] * inv_w);
-          store8(po + 32 * dc + 8 * i, __builtin_bit_cast(uint2, vv));
-        }
+      store_tile(o, 1.f / ww, [&](int ps) -> bf16* {
+        return ps < cd.count ? a.out + ((static_cast<int64_t>(cd.b) * a.B + cd.start + ps) * a.H + cd.h) * D
+                             : a.part_diag + (static_cast<int64_t>(a.H) * a.N + ps) * D;
+      });
       store4(valid ? a.lse_out + static_cast<int64_t>(cd.h) * a.N + tok
                    : a.lse_diag + static_cast<int64_t>(a.H) * a.N + pos,
              (mm + log2f(ww)) * kLn2);
@@ -833,23 +871,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
       const float l_tot = l + __shfl_xor(l, 32);
       const float inv_l = 1.f / l_tot;
       const int pos = pos0 + qn;
-      const bool valid = pos < cd.count;
-      int64_t row;
-      if (kCausal)
-        row = valid ? static_cast<int64_t>(cd.h) * a.N + static_cast<int64_t>(cd.b) * a.B + cd.start + pos
-                    : static_cast<int64_t>(a.H) * a.N + pos;
-      else
-        row = valid ? static_cast<int64_t>(cd.start) + pos : a.p_off + pos;
-      bf16* po = (kCausal ? a.part_diag : a.part_off) + row * D + 4 * half;
-#pragma unroll
-      for (int dc = 0; dc < kDC; ++dc)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          bf16x4 vv;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) vv[e] = static_cast<bf16>(o[dc][4 * i + e] * inv_l);
-          store8(po + 32 * dc + 8 * i, __builtin_bit_cast(uint2, vv));
-        }
+      // Output row of item position ps: the item's list entries (past
+      // blocks) or queries (own block); slots without one write to dump rows.
+      auto row_of = [&](int ps) -> int64_t {
+        if (kCausal)
+          return ps < cd.count ? static_cast<int64_t>(cd.h) * a.N + static_cast<int64_t>(cd.b) * a.B + cd.start + ps
+                               : static_cast<int64_t>(a.H) * a.N + ps;
+        return ps < cd.count ? static_cast<int64_t>(cd.start) + ps : a.p_off + ps;
+      };
+      store_tile(o, inv_l, [&](int ps) -> bf16* { return (kCausal ? a.part_diag : a.part_off) + row_of(ps) * D; });
+      const int64_t row = row_of(pos);
       store4((kCausal ? a.lse_diag : a.lse_off) + row, (m * c2 + log2f(l_tot)) * kLn2);
     }
     sh1 = 1;
