@@ -427,6 +427,41 @@ __device__ __forceinline__ void tile_pair(const char* kp, const char* vp, const 
   pv<D>(va1, p1, o);
 }
 
+// Past-block tiles (no mask), pipelined across ring steps: the PV of a
+// tile's second half runs at the start of the next step, from probabilities
+// and V^T operands kept in registers, so that each step opens with MFMAs
+// that need no LDS read while the K reads of the new tile are in flight:
+//   PV(t-1, h1) + S(t, h0) | S(t, h1) + softmax(t, h0) | PV(t, h0) + softmax(t, h1).
+// p1 is zero on an item's first tile (the PV then adds exactly zero).
+template <int D, typename F>
+__device__ __forceinline__ void tile_step(const char* kp, const char* vp, const bf16x8 (&q)[D / 16],
+                                          f32x16 (&o)[D / 32], float& m, float& l, float c2, bf16x8 (&p1)[2],
+                                          bf16x8 (&va1)[D / 32][2], F&& issue) {
+  using L = Lay<D>;
+  constexpr int kQC = D / 16;
+  pv<D>(va1, p1, o);
+  f32x16 s0 = scores<D>(kp, q);
+  __builtin_amdgcn_sched_barrier(0);
+  issue(0);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 s1 = scores<D>(kp + 32 * L::kKStride, q);
+  bf16x8 p0[2], va0[D / 32][2];
+  float lh0 = probs(s0, c2, m * c2, p0);
+  v_operands<D>(vp, va0);
+  interleave<kQC, 3, 6>();
+  settle<D>(s0, m, l, o, p0, lh0, c2);
+  l += lh0;
+  __builtin_amdgcn_sched_barrier(0);
+  issue(1);
+  __builtin_amdgcn_sched_barrier(0);
+  pv<D>(va0, p0, o);
+  float lh1 = probs(s1, c2, m * c2, p1);
+  v_operands<D>(vp + 32 * L::kVStride, va1);
+  interleave<2 * (D / 32), 2, 6>();
+  settle<D>(s1, m, l, o, p1, lh1, c2);
+  l += lh1;
+}
+
 // One half only (own-block items: the tile whose first half holds the diagonal).
 template <int D>
 __device__ __forceinline__ void tile_first_half(const char* kp, const char* vp, const bf16x8 (&q)[D / 16],
@@ -754,6 +789,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
     }
   };
 
+  bf16x8 p1[2], va1[kDC][2];
+#pragma unroll
+  for (int dc = 0; dc < kDC; ++dc)
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) va1[dc][g][e] = static_cast<bf16>(0.f);
+
   for (int mc = 0; mc < cnt; ++mc) {
     const Desc cd = item_desc<kCausal, kFused>(a, first + static_cast<int64_t>(mc) * stride);
     bf16x8 q[kQC];
@@ -785,6 +828,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
     const bool wave_valid = pos0 < cd.count;
     const int f = cd.start + pos0;                 // own-block items: block position of the first query
     const int qpos = f + qn;
+    // Past-block items: probabilities and V^T operands of the previous
+    // tile's second half (its PV runs in the next step).
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p1[g][e] = static_cast<bf16>(0.f);
     for (int t = 0; t < cd.nkt; ++t) {
       const int kbase = t * kKTile;
       const char* slot = ring_step(-1, cd, true);
@@ -794,7 +843,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
         if (part == 0) load_part(now, sl, 0, kSplit);
         else load_part(now, sl, kSplit, L::kRoundsHi);
       };
-      if (wave_valid && (!kCausal || kbase < f)) {
+      if (!kCausal && wave_valid) {
+        tile_step<D>(slot + k_lane, slot + v_lane, q, o, m, l, c2, p1, va1, issue);
+      } else if (wave_valid && (!kCausal || kbase < f)) {
         // Both halves visible (the second may hold the diagonal).
         tile_pair<D>(slot + k_lane, slot + v_lane, q, o, m, l, kCausal && kbase + 32 == f, kbase + 32, qpos, half,
                      c2, issue);
@@ -804,6 +855,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
           tile_first_half<D>(slot + k_lane, slot + v_lane, q, o, m, l, kbase, qpos, half, c2);
       }
     }
+    if (!kCausal && wave_valid) pv<D>(va1, p1, o);   // the last tile's second half
     // ---- epilogue: normalise and store the item's partial rows ----
     if (kFused) {
       // LSE merge with the query's past-block partials (natural-log lse_s,
