@@ -127,10 +127,9 @@ constexpr int kQTileRows = kAttnTile / 2;  // queries per Q tile (the first or l
 constexpr int kQBuf = 2 * kAttnTile;       // query-index entries per buffer (one 4-byte load per lane)
 // Own-block items with the merge fused in: list positions of the item's past
 // selections, [query][lmax], loaded into LDS in kInvRounds 4-byte loads per lane.
-constexpr int kFusedMaxPast = 8;
+constexpr int kFusedMaxPast = 16;
 constexpr int kInvInts = kAttnTile * kFusedMaxPast;
 constexpr int kInvRounds = kInvInts / (kWaves * kWave);
-constexpr int kTailBytes = (2 * kQBuf * 4 > kInvInts * 4) ? 2 * kQBuf * 4 : kInvInts * 4;
 
 // LDS image of one ring slot. A slot holds either one 64-key tile of K and V
 // (row-major, keys on rows) or 128 query rows. Rows are padded so that the
@@ -513,6 +512,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
   constexpr int kXq = kCausal ? (kFused ? kInvRounds : 0) : 1;
   static_assert(!kFused || kCausal, "the merge is fused into own-block items only");
   static_assert((kAhead - 1) * L::kRoundsHi + kStoresPerItem + kXq < 64, "vmcnt holds at most 63");
+  // Tail buffer: the double-buffered query indices (past-block items) or the
+  // list positions of the item's past selections (fused own-block items).
+  constexpr int kTailBytes = kFused ? kInvInts * 4 : 2 * kQBuf * 4;
   __shared__ __attribute__((aligned(16))) char smem[kSlots * L::kSlot + kWaves * kStageBytes + kTailBytes];
   char* const ring = smem;
   char* const stage = smem + kSlots * L::kSlot;

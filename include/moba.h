@@ -125,7 +125,7 @@ int moba_prefill_fwd_f32(const float* q, const float* k, const float* v, float* 
  *   0 before the block mean-pool, 1 before the gate/top-k, 2 before the query
  *   lists, 3 before the past-block attention, 4 before the own-block
  *   attention (which also performs the LSE merge when every query keeps at
- *   most 8 past blocks on the bf16 path), 5 before the separate merge (an
+ *   most 16 past blocks on the bf16 path), 5 before the separate merge (an
  *   empty stage when it was fused), 6 after it. The fp32 path runs the whole
  *   block attention in the past-block stage (the own-block stage is empty).
  * hipEventElapsedTime between neighbours gives each stage's device time.
