@@ -50,6 +50,43 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
+// Per-lane running top-KCAP of (score, block), best first, for the bf16
+// path: blocks arrive in increasing order within a lane, so a plain
+// "strictly greater" test leaves equal scores in block order (lower block
+// first), as the ranking requires. Empty slots hold -inf. -0 and +0 compare
+// equal, as in the orderable key.
+template <int KCAP>
+struct ScoreList {
+  float s[KCAP];
+  int b[KCAP];
+  __device__ __forceinline__ void clear() {
+#pragma unroll
+    for (int i = 0; i < KCAP; ++i) {
+      s[i] = -INFINITY;
+      b[i] = 0;
+    }
+  }
+  // Insert a block later in order than every block already held.
+  __device__ __forceinline__ void push(float x, int blk) {
+    bool gt[KCAP];
+#pragma unroll
+    for (int i = 0; i < KCAP; ++i) gt[i] = x > s[i];
+#pragma unroll
+    for (int i = KCAP - 1; i > 0; --i) {
+      s[i] = gt[i - 1] ? s[i - 1] : (gt[i] ? x : s[i]);
+      b[i] = gt[i - 1] ? b[i - 1] : (gt[i] ? blk : b[i]);
+    }
+    s[0] = gt[0] ? x : s[0];
+    b[0] = gt[0] ? blk : b[0];
+  }
+  // The 64-bit ranking keys (0 for empty slots), merged with the lane 32
+  // away, which holds the other blocks of the same query.
+  __device__ __forceinline__ void to_keys(uint64_t (&list)[KCAP]) const {
+#pragma unroll
+    for (int i = 0; i < KCAP; ++i) list[i] = s[i] > -INFINITY ? rank_key(s[i], b[i]) : 0ull;
+  }
+};
+
 template <int KCAP>
 __device__ __forceinline__ void merge_with_partner(uint64_t (&list)[KCAP]) {
   uint64_t other[KCAP];
@@ -195,6 +232,8 @@ __global__ __launch_bounds__(256) void gate_mfma_kernel(const bf16* __restrict__
 #pragma unroll
     for (int s = 0; s < KCAP; ++s) list[s] = 0;
     if (jw >= a.topk && a.topk > 1 && t0w < a.N) {
+      ScoreList<KCAP> sl;
+      sl.clear();
       for (int bc = 0; bc * 32 < jw; ++bc) {
         f32x16 acc;
 #pragma unroll
@@ -213,9 +252,10 @@ __global__ __launch_bounds__(256) void gate_mfma_kernel(const bf16* __restrict__
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int b = bc * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          topk_insert<KCAP>(list, b < j ? rank_key(acc[r], b) : 0ull);
+          sl.push(b < j ? acc[r] : -INFINITY, b);
         }
       }
+      sl.to_keys(list);
       merge_with_partner<KCAP>(list);
     }
     finalize<KCAP>(a, list, t, valid, j, bmb + buf * 4 * n, tile);
