@@ -128,29 +128,42 @@ STAGE_EVENTS = len(STAGES) + 1
 
 
 class StageEvents:
-    """HIP events the library records at its stage boundaries (bf16 prefill)."""
+    """HIP events the library records at its stage boundaries (bf16 prefill).
 
-    def __init__(self):
+    ``stages`` limits the recorded boundaries to those around the named stages
+    (the others are passed as NULL and not recorded); their times accumulate
+    in ``totals``, the other stages stay at zero."""
+
+    def __init__(self, stages=STAGES):
         self._hip = ctypes.CDLL("libamdhip64.so")
         self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.stages = tuple(stages)
+        wanted = set()
+        for s in self.stages:
+            i = STAGES.index(s)
+            wanted.update((i, i + 1))
         self.array = (ctypes.c_void_p * STAGE_EVENTS)()
         for i in range(STAGE_EVENTS):
-            ev = ctypes.c_void_p()
-            if self._hip.hipEventCreate(ctypes.byref(ev)) != 0:
-                raise RuntimeError("hipEventCreate failed")
-            self.array[i] = ev
+            self.array[i] = None
+            if i in wanted:
+                ev = ctypes.c_void_p()
+                if self._hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                    raise RuntimeError("hipEventCreate failed")
+                self.array[i] = ev
         self.totals = {s: 0.0 for s in STAGES}
         self.calls = 0
 
     def accumulate(self):
         """Wait for the last recorded call and add its stage times (ms)."""
-        if self._hip.hipEventSynchronize(self.array[STAGE_EVENTS - 1]) != 0:
+        last = max(i for i in range(STAGE_EVENTS) if self.array[i])
+        if self._hip.hipEventSynchronize(self.array[last]) != 0:
             raise RuntimeError("hipEventSynchronize failed")
         ms = ctypes.c_float()
-        for i, s in enumerate(STAGES):
+        for s in self.stages:
+            i = STAGES.index(s)
             if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.array[i], self.array[i + 1]) != 0:
                 raise RuntimeError("hipEventElapsedTime failed")
             self.totals[s] += ms.value
@@ -161,7 +174,8 @@ class StageEvents:
 
     def close(self):
         for i in range(STAGE_EVENTS):
-            self._hip.hipEventDestroy(self.array[i])
+            if self.array[i]:
+                self._hip.hipEventDestroy(self.array[i])
 
 
 def prefill(q, k, v, block_size: int, topk: int, out=None, lse=None, events: "StageEvents | None" = None):

@@ -242,7 +242,7 @@ int prefill_impl(const void* q, const void* k, const void* v, void* out, float* 
   char* base = nullptr;
   if ((s = alloc_ws(st, w.total, stream, &base)) != MOBA_OK) return s;
   moba::Workspace ws = bind(w, base, true);
-  auto mark = [&](int i) { return events ? hipEventRecord(events[i], stream) : hipSuccess; };
+  auto mark = [&](int i) { return events && events[i] ? hipEventRecord(events[i], stream) : hipSuccess; };
   hipError_t e = mark(0);
   if (e == hipSuccess) e = moba::launch_pool(k, is_f32, ws.kbar, is_f32 ? nullptr : ws.kpieces, N, H, D, B, stream);
   if (e == hipSuccess) e = mark(1);

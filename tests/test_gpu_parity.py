@@ -154,6 +154,28 @@ def test_deterministic(moba):
     assert torch.equal(s1, s2)
 
 
+def test_stage_events(moba):
+    """The timed entry point: same results with all, some or no stage events."""
+    N, H, D, B, topk = 4096, 2, 128, 256, 3
+    q, k, v = synth.make_qkv(N, H, D, seed=[104, 0], dtype="bf16")
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    o1, l1 = moba.prefill(qd, kd, vd, B, topk)
+    full = moba.StageEvents()
+    o2, l2 = moba.prefill(qd, kd, vd, B, topk, events=full)
+    part = moba.StageEvents(stages=("attn_past",))
+    o3, l3 = moba.prefill(qd, kd, vd, B, topk, events=part)
+    torch.cuda.synchronize()
+    full.accumulate()
+    part.accumulate()
+    for o, l in ((o2, l2), (o3, l3)):
+        assert torch.equal(o1.view(torch.int16), o.view(torch.int16))
+        assert torch.equal(l1.view(torch.int32), l.view(torch.int32))
+    assert all(full.totals[s] >= 0.0 for s in moba.STAGES) and full.totals["attn_past"] > 0.0
+    assert part.totals["attn_past"] > 0.0 and part.totals["gate"] == 0.0
+    full.close()
+    part.close()
+
+
 def test_bad_arguments_leave_outputs_untouched(moba):
     N, H, D = 1024, 1, 128
     q = torch.zeros(N, H, D, dtype=torch.bfloat16, device="cuda")
