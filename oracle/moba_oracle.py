@@ -42,6 +42,11 @@ Readings of points the pages leave open (each one is listed in the design notes)
   to fp32. Everything else (the attention, the log-sum-exp) is fp64.
 * The softmax scale is 1/√D; lse is the natural log of the sum of
   exp(q·k/√D) over A(t).
+
+``moba_decode_ref`` is the generation step after the prefill: the newest token
+(position N - 1 of a cache whose length need not be a multiple of B, so its
+own block may be partial) gated and attended exactly like a prefill row; with
+top_k above the number of past blocks it is full attention.
 """
 
 from __future__ import annotations
@@ -309,3 +314,48 @@ def attended_pairs_closed_form(N: int, block_size: int, topk: int) -> int:
 def sparsity(N: int, block_size: int, topk: int) -> float:
     """Fraction of the context a late query does not attend: 1 - B*k/N."""
     return 1.0 - block_size * min(topk, n_blocks(N, block_size)) / N
+
+
+def moba_decode_ref(q_new, k, v, block_size: int, topk: int, kbar32=None, sel=None):
+    """fp64 MoBA decode step: the newest token attends its selected blocks.
+
+    The generation step after the prefill (wzjinhao.cn MoBA article, section 3:
+    decoding may switch back to full attention; the MoBA form gates the new
+    token exactly like a prefill row). ``q_new`` is [H, D], the query of the
+    token at position t = N - 1, whose key and value are already the last rows
+    of the cache ``k``, ``v`` [N, H, D]; N need not be a multiple of B, so the
+    token's own block j = floor(t / B) may be partial (keys jB .. t).
+
+    Gate: the fp32 mean keys of the complete past blocks 0 .. j-1 (``kbar32``
+    [H, >= j, D] if given, else the exact mean rounded once to fp32), fp32
+    scores, then the same causal top-k as a prefill row (``select_row``).
+    top_k > j selects every past block: full causal attention for the token.
+
+    Returns ``(out [H, D] fp64, lse [H] fp64 natural log, sel [H, topk] int32)``.
+    """
+    k = np.asarray(k)
+    N, H, D = k.shape
+    if N < 1 or block_size < 1 or topk < 1:
+        raise ValueError("need N >= 1, block_size >= 1, topk >= 1")
+    t = N - 1
+    j = t // block_size
+    if sel is None:
+        if kbar32 is None and j > 0:
+            kbar32 = pooled_keys_fp32(k[:j * block_size], block_size)
+        sel = np.full((H, topk), -1, dtype=np.int32)
+        for h in range(H):
+            scores = gate_scores(np.asarray(q_new)[h][None, :], kbar32[h, :j])[0] if j > 0 else np.zeros(0, np.float32)
+            row = select_row(scores, j, topk)
+            sel[h, :len(row)] = row
+    inv_sqrt_d = 1.0 / math.sqrt(D)
+    out = np.zeros((H, D), np.float64)
+    lse = np.zeros(H, np.float64)
+    for h in range(H):
+        keys = attended_keys(sel[h], t, block_size)
+        k_att = np.asarray(k[keys, h, :], np.float64)
+        v_att = np.asarray(v[keys, h, :], np.float64)
+        logits = (k_att @ np.asarray(q_new[h], np.float64)) * inv_sqrt_d
+        p, l = _softmax_rows(logits[None, :])
+        out[h] = p[0] @ v_att
+        lse[h] = l[0]
+    return out, lse, sel

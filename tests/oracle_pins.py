@@ -336,9 +336,107 @@ def pin_row_mode_matches(m):
         assert np.allclose(l3, lse, atol=1e-13, rtol=0)
 
 
+# ---------------------------------------------------------------------------
+# decode step (one new token at position N - 1; N need not be a multiple of B)
+# ---------------------------------------------------------------------------
+
+def _sdpa_one(qv, kk, vv):
+    """Attention of one query over the given keys through torch SDPA (fp64), and its logsumexp."""
+    qh, kh, vh = _t64(qv)[None, None], _t64(kk)[None], _t64(vv)[None]
+    o = torch.nn.functional.scaled_dot_product_attention(qh, kh, vh)[0, 0].numpy()
+    lse = float(torch.logsumexp((kh[0] @ qh[0, 0]) / math.sqrt(qv.shape[-1]), dim=0))
+    return o, lse
+
+
+def pin_decode_full_attention(m):
+    """top_k above the number of past blocks: the token attends the whole cache."""
+    for N, H, D, B, seed in [(77, 2, 8, 16, 161), (64, 1, 8, 16, 162), (5, 2, 4, 8, 163), (130, 1, 4, 64, 164)]:
+        q, k, v = _rand(N, H, D, seed)
+        out, lse, sel = m.moba_decode_ref(q[N - 1], k, v, B, (N - 1) // B + 2)
+        for h in range(H):
+            ro, rl = _sdpa_one(q[N - 1, h], k[:, h], v[:, h])
+            assert np.allclose(out[h], ro, atol=1e-12, rtol=0)
+            assert abs(lse[h] - rl) < 1e-12
+            assert list(sel[h][sel[h] >= 0]) == list(range((N - 1) // B + 1))
+
+
+def pin_decode_own_block(m):
+    """top_k = 1: only the token's own (possibly partial) block, keys jB .. N-1."""
+    for N, H, D, B, seed in [(77, 2, 8, 16, 171), (64, 1, 8, 16, 172), (100, 2, 4, 32, 173)]:
+        q, k, v = _rand(N, H, D, seed)
+        out, lse, sel = m.moba_decode_ref(q[N - 1], k, v, B, 1)
+        j0 = ((N - 1) // B) * B
+        for h in range(H):
+            ro, rl = _sdpa_one(q[N - 1, h], k[j0:, h], v[j0:, h])
+            assert np.allclose(out[h], ro, atol=1e-12, rtol=0)
+            assert abs(lse[h] - rl) < 1e-12
+
+
+def pin_decode_first_token(m):
+    q, k, v = _rand(1, 2, 8, 181)
+    out, lse, sel = m.moba_decode_ref(q[0], k, v, 16, 3)
+    for h in range(2):
+        assert np.array_equal(out[h], v[0, h].astype(np.float64))
+        assert abs(lse[h] - float(np.dot(q[0, h].astype(np.float64), k[0, h].astype(np.float64))) / math.sqrt(8)) < 1e-13
+    assert np.array_equal(sel, np.array([[0, -1, -1], [0, -1, -1]]))
+
+
+def pin_decode_brute_selection(m):
+    """The gate of a decode step against exhaustive subset search over the
+    complete past blocks (fp32 means and scores through torch)."""
+    for N, H, D, B, topk, seed in [(45, 2, 4, 4, 3, 191), (37, 1, 4, 2, 4, 192), (64, 2, 4, 8, 2, 193), (9, 1, 4, 2, 5, 194)]:
+        q, k, v = _rand(N, H, D, seed)
+        out, lse, sel = m.moba_decode_ref(q[N - 1], k, v, B, topk)
+        t = N - 1
+        j = t // B
+        for h in range(H):
+            if j + 1 <= topk:
+                want = list(range(j + 1))
+            else:
+                kbar = _t64(k[:j * B, h]).reshape(j, B, D).mean(dim=1).to(torch.float32).to(torch.float64)
+                sc = (kbar @ _t64(q[t, h])).to(torch.float32).to(torch.float64).numpy()
+                best, best_sum = None, -math.inf
+                for comb in itertools.combinations(range(j), topk - 1):
+                    s = sum(sc[i] for i in comb)
+                    if s > best_sum:
+                        best, best_sum = comb, s
+                want = sorted(list(best) + [j])
+            assert list(sel[h][sel[h] >= 0]) == want, (N, B, topk, h)
+        bo, bl = brute_attention_rows(q, k, v, B, sel, t)
+        assert np.allclose(out, bo, atol=1e-12, rtol=0)
+        assert np.allclose(lse, bl, atol=1e-12, rtol=0)
+
+
+def brute_attention_rows(q, k, v, B, sel_t, t):
+    """Attention of row t over the keys of its chosen blocks (token by token mask), through SDPA."""
+    N, H, D = k.shape
+    out = np.zeros((H, D))
+    lse = np.zeros(H)
+    for h in range(H):
+        chosen = set(int(x) for x in sel_t[h] if x >= 0)
+        keys = [s for s in range(t + 1) if s // B in chosen]
+        out[h], lse[h] = _sdpa_one(q[t, h], k[keys, h], v[keys, h])
+    return out, lse
+
+
+def pin_decode_matches_prefill_row(m):
+    """With B dividing N, the decode step is the prefill's last row."""
+    for N, H, D, B, topk, seed in [(64, 2, 8, 8, 3, 201), (96, 1, 8, 16, 2, 202), (128, 2, 4, 16, 5, 203)]:
+        q, k, v = _rand(N, H, D, seed)
+        out, lse, sel = m.moba_decode_ref(q[N - 1], k, v, B, topk)
+        po, pl, ps = m.moba_ref(q, k, v, B, topk, rows=np.array([N - 1]))
+        assert np.array_equal(sel, ps[:, 0])
+        assert np.allclose(out, po[0], atol=1e-13, rtol=0)
+        assert np.allclose(lse, pl[:, 0], atol=1e-13, rtol=0)
+        kbar = m.pooled_keys_fp32(k, B)
+        o2, l2, s2 = m.moba_decode_ref(q[N - 1], k, v, B, topk, kbar32=kbar)
+        assert np.array_equal(s2, sel) and np.array_equal(o2, out) and np.array_equal(l2, lse)
+
+
 ALL_PINS = [
     pin_bruteforce_tiny, pin_full_causal, pin_block_diagonal, pin_first_token, pin_constant_v,
     pin_zero_query, pin_invariants, pin_pages_worked_example, pin_pages_sparsity_table,
     pin_granularity, pin_closed_form_pairs, pin_lse_merge, pin_pooling_linearity,
-    pin_gate_rounding, pin_row_mode_matches,
+    pin_gate_rounding, pin_row_mode_matches, pin_decode_full_attention, pin_decode_own_block,
+    pin_decode_first_token, pin_decode_brute_selection, pin_decode_matches_prefill_row,
 ]

@@ -54,6 +54,13 @@ MUTATIONS = {
     "blocks_drops_denominator_terms": ("l[ridx] += p.sum(axis=1)", "l[ridx] = p.sum(axis=1)"),
     "rowwise_wrong_head": ("kh = np.asarray(k[keys, h, :], np.float64)",
                            "kh = np.asarray(k[keys, (h + 1) % H, :], np.float64)"),
+    "decode_token_off_by_one": ("    t = N - 1\n    j = t // block_size\n    if sel is None:",
+                                "    t = N - 1\n    j = t // block_size\n    t = max(t - 1, 0)\n    if sel is None:"),
+    "decode_means_reversed": ("kbar32 = pooled_keys_fp32(k[:j * block_size], block_size)",
+                                   "kbar32 = pooled_keys_fp32(k[:j * block_size], block_size)[:, ::-1]"),
+    "decode_wrong_query_head": ("logits = (k_att @ np.asarray(q_new[h], np.float64)) * inv_sqrt_d",
+                                "logits = (k_att @ np.asarray(q_new[(h + 1) % H], np.float64)) * inv_sqrt_d"),
+    "decode_scale_1_over_d": ("inv_sqrt_d = 1.0 / math.sqrt(D)", "inv_sqrt_d = 1.0 / D"),
 }
 
 
