@@ -38,6 +38,7 @@ _SIGNATURES = {
     "moba_prefill_fwd": [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P],
     "moba_prefill_fwd_f32": [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P],
     "moba_prefill_fwd_timed": [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P],
+    "moba_decode_fwd": [_P, _P, _P, _P, _I32, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P],
     "moba_status_string": [ctypes.c_int],
     "moba_last_hip_error": [],
 }
@@ -203,4 +204,43 @@ def prefill(q, k, v, block_size: int, topk: int, out=None, lse=None, events: "St
     fn = lib.moba_prefill_fwd_f32 if f32 else lib.moba_prefill_fwd
     _check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), N, H, D, block_size, topk,
               _stream(q.device)), "moba_prefill_fwd")
+    return out, lse
+
+
+def decode(q_new, k, v, block_size: int, topk: int, kbar=None, out=None, lse=None, sel=None):
+    """MoBA decode step (bf16) for the token at position N - 1 of the cache.
+
+    ``q_new`` [H, D]; ``k``, ``v`` [N, H, D] (the token's own key and value are
+    the last rows); ``kbar`` optional fp32 [H, nb, D] block means of the
+    complete blocks (nb >= (N - 1) // block_size), e.g. from
+    :func:`block_mean_keys` over the complete prefix. Returns
+    ``(out [H, D] bf16, lse [H] fp32)``; ``sel`` (int32 [H, topk]) receives
+    the kept blocks when given."""
+    import torch
+    if k.dim() != 3 or k.dtype != torch.bfloat16 or not k.is_cuda:
+        raise ValueError("k must be a bf16 [N, H, D] GPU tensor")
+    N, H, D = k.shape
+    for t in (k, v):
+        if t.shape != k.shape or t.dtype != k.dtype or t.device != k.device or not t.is_contiguous():
+            raise ValueError("k and v must be contiguous bf16 [N, H, D] tensors on one device")
+    if q_new.shape != (H, D) or q_new.dtype != torch.bfloat16 or q_new.device != k.device or not q_new.is_contiguous():
+        raise ValueError("q_new must be a contiguous bf16 [H, D] tensor on the cache's device")
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q_new)
+    if lse is None:
+        lse = torch.empty((H,), dtype=torch.float32, device=k.device)
+    kb, nb = 0, 0
+    if kbar is not None:
+        if kbar.dim() != 3 or kbar.shape[0] != H or kbar.shape[2] != D or kbar.dtype != torch.float32 \
+                or not kbar.is_contiguous():
+            raise ValueError("kbar must be a contiguous fp32 [H, nb, D] tensor")
+        kb, nb = kbar.data_ptr(), kbar.shape[1]
+    sp = 0
+    if sel is not None:
+        if sel.shape != (H, topk) or sel.dtype != torch.int32 or not sel.is_contiguous():
+            raise ValueError("sel must be a contiguous int32 [H, topk] tensor")
+        sp = sel.data_ptr()
+    _check(lib.moba_decode_fwd(q_new.data_ptr(), k.data_ptr(), v.data_ptr(), kb, nb, out.data_ptr(), lse.data_ptr(),
+                               sp, N, H, D, block_size, topk, _stream(k.device)), "moba_decode_fwd")
     return out, lse

@@ -3,6 +3,8 @@
 // point only enqueues on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <mutex>
 
@@ -257,6 +259,64 @@ int prefill_impl(const void* q, const void* k, const void* v, void* out, float* 
   return finish(e, base, stream);
 }
 
+int decode_impl(const void* q, const void* k, const void* v, const float* kbar, int32_t kbar_blocks, void* out,
+                float* lse, int32_t* sel, int64_t N, int32_t H, int32_t D, int32_t B, int32_t topk,
+                hipStream_t stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || lse == nullptr) return MOBA_ERR_INVALID_ARG;
+  if (N < 1 || H < 1 || B < 1 || topk < 1) return MOBA_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return MOBA_ERR_UNSUPPORTED;
+  if (N >= (int64_t{1} << 40) || H > 65535) return MOBA_ERR_UNSUPPORTED;
+  const int64_t j = (N - 1) / B;   // the new token's block; blocks 0..j-1 are complete
+  if (j >= (int64_t{1} << 24)) return MOBA_ERR_UNSUPPORTED;
+  if (topk > MOBA_MAX_TOPK && topk <= j) return MOBA_ERR_UNSUPPORTED;
+  if (sel != nullptr && topk > MOBA_MAX_BLOCKS) return MOBA_ERR_UNSUPPORTED;
+  if (kbar != nullptr && kbar_blocks < j) return MOBA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse) ||
+      (kbar != nullptr && !aligned16(kbar)) || (sel != nullptr && !aligned16(sel)))
+    return MOBA_ERR_UNSUPPORTED;
+  int s;
+  DeviceState* st = nullptr;
+  if ((s = current_device(&st)) != MOBA_OK) return s;
+  moba::DecodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.N = N;
+  a.H = H;
+  a.D = D;
+  a.B = B;
+  a.j = static_cast<int>(j);
+  a.topk = topk;
+  a.S = static_cast<int>(std::min<int64_t>(topk, j + 1));
+  a.chunks = (B + moba::kDecChunk - 1) / moba::kDecChunk;
+  a.units = a.S * a.chunks;
+  a.scale_log2 = 1.4426950408889634f / std::sqrt(static_cast<float>(D));
+  const bool own_kbar = kbar == nullptr && j > 0;
+  Layout L;
+  const size_t o_sel = L.add(static_cast<size_t>(H) * a.S * 4);
+  const size_t o_sc = L.add(static_cast<size_t>(H) * j * 4);
+  const size_t o_po = L.add(static_cast<size_t>(H) * a.units * D * 4);
+  const size_t o_ml = L.add(static_cast<size_t>(H) * a.units * 2 * 4);
+  const size_t o_kb = L.add(own_kbar ? static_cast<size_t>(H) * j * D * 4 : 0);
+  char* base = nullptr;
+  if ((s = alloc_ws(st, L.total, stream, &base)) != MOBA_OK) return s;
+  a.q = static_cast<const moba::bf16*>(q);
+  a.k = static_cast<const moba::bf16*>(k);
+  a.v = static_cast<const moba::bf16*>(v);
+  a.kbar = own_kbar ? reinterpret_cast<const float*>(base + o_kb) : kbar;
+  a.kbar_blocks = own_kbar ? static_cast<int>(j) : kbar_blocks;
+  a.sel = reinterpret_cast<int32_t*>(base + o_sel);
+  a.sel_out = sel;
+  a.scores = reinterpret_cast<float*>(base + o_sc);
+  a.part_o = reinterpret_cast<float*>(base + o_po);
+  a.part_ml = reinterpret_cast<float*>(base + o_ml);
+  a.out = static_cast<moba::bf16*>(out);
+  a.lse = lse;
+  hipError_t e = hipSuccess;
+  if (own_kbar)
+    e = moba::launch_pool(k, false, reinterpret_cast<float*>(base + o_kb), nullptr, j * B, H, D, B, stream);
+  if (e == hipSuccess) e = moba::launch_decode(a, stream);
+  return finish(e, base, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -294,6 +354,12 @@ int moba_prefill_fwd_timed(const void* q, const void* k, const void* v, void* ou
 int moba_prefill_fwd_f32(const float* q, const float* k, const float* v, float* out, float* lse, int64_t N, int32_t H,
                          int32_t D, int32_t block_size, int32_t topk, hipStream_t stream) {
   return prefill_impl(q, k, v, out, lse, N, H, D, block_size, topk, stream, true);
+}
+
+int moba_decode_fwd(const void* q, const void* k, const void* v, const float* kbar, int32_t kbar_blocks, void* out,
+                    float* lse, int32_t* sel, int64_t N, int32_t H, int32_t D, int32_t block_size, int32_t topk,
+                    hipStream_t stream) {
+  return decode_impl(q, k, v, kbar, kbar_blocks, out, lse, sel, N, H, D, block_size, topk, stream);
 }
 
 const char* moba_status_string(int status) {

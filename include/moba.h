@@ -137,6 +137,36 @@ int moba_prefill_fwd_timed(const void* q, const void* k, const void* v, void* ou
                            int64_t N, int32_t H, int32_t D, int32_t block_size, int32_t topk,
                            hipStream_t stream, hipEvent_t* events);
 
+/*
+ * MoBA decode step (bf16): the newest token of a K/V cache attends its gated
+ * blocks. After the prefill, generation adds one token at a time; the
+ * wzjinhao.cn MoBA article (section 3) runs that step as full attention or
+ * gated like a prefill row. The token's key and value must already be the
+ * last rows of the cache, so the token sits at position t = N - 1, in block
+ * j = floor(t / B); N need not be a multiple of B (the own block may be
+ * partial). Its gate scores the fp32 means of the complete past blocks
+ * 0 .. j-1 exactly like moba_gate_topk scores a prefill row (no scale,
+ * ranking by score then lower block index), keeps the topk - 1 best and its
+ * own block; topk > j keeps every block (full attention over the cache).
+ *   q: bf16 [H][D], the new token's query.   k, v: bf16 [N][H][D] cache.
+ *   kbar: fp32 [H][kbar_blocks][D] block means of the cache's complete blocks
+ *         as moba_block_mean_keys writes them (at least j blocks per head,
+ *         kbar_blocks >= j); NULL makes the call compute them from k (one
+ *         pass over the first j*B rows).
+ *   out: bf16 [H][D].   lse: fp32 [H], natural log of the softmax
+ *         denominator.   sel: NULL, or int32 [H][topk] receiving the kept
+ *         blocks in ascending order, -1 padded.
+ * Errors: MOBA_ERR_INVALID_ARG for null q/k/v/out/lse, N, H, block_size or
+ * topk < 1, kbar_blocks < j with kbar given; MOBA_ERR_UNSUPPORTED for D not
+ * 64/128, topk in (MOBA_MAX_TOPK, j], sel with topk > MOBA_MAX_BLOCKS,
+ * pointers not 16-byte aligned, not gfx950. Nothing is enqueued on error.
+ * Enqueues on `stream` and returns; the workspace comes from the same
+ * stream-ordered pool as the prefill.
+ */
+int moba_decode_fwd(const void* q, const void* k, const void* v, const float* kbar, int32_t kbar_blocks,
+                    void* out, float* lse, int32_t* sel, int64_t N, int32_t H, int32_t D,
+                    int32_t block_size, int32_t topk, hipStream_t stream);
+
 /* Static, NUL-terminated name of a status code ("MOBA_OK", ...). */
 const char* moba_status_string(int status);
 

@@ -133,3 +133,28 @@ def test_python_binding_rejects_bad_tensors():
         moba.prefill(q.half(), q.half(), q.half(), 64, 3)
     with pytest.raises(ValueError):
         moba.gate_topk(q[0], q[0], 64, 3)
+
+
+def decode(lib, N=1000, H=2, D=128, B=128, topk=3, ptrs=(A, A, A, A, A), kbar=None, nb=0, sel=None):
+    q, k, v, out, lse = ptrs
+    return lib.moba_decode_fwd(q, k, v, kbar, nb, out, lse, sel, N, H, D, B, topk, None)
+
+
+def test_decode_argument_checks(lib):
+    for i in range(5):
+        ptrs = [A] * 5
+        ptrs[i] = None
+        assert decode(lib, ptrs=tuple(ptrs)) == INVALID
+    for kw in (dict(N=0), dict(H=0), dict(B=0), dict(topk=0), dict(topk=-2)):
+        assert decode(lib, **kw) == INVALID, kw
+    # kbar given with fewer blocks than the token's complete past blocks (999 // 128 = 7)
+    assert decode(lib, kbar=A, nb=6) == INVALID
+    for kw in (dict(D=96), dict(D=32), dict(H=70000), dict(N=128 * 100, topk=40)):
+        assert decode(lib, **kw) == UNSUPPORTED, kw
+    assert decode(lib, sel=A, topk=5000, N=128) == UNSUPPORTED
+    for i in range(5):
+        ptrs = [A] * 5
+        ptrs[i] = A + 4
+        assert decode(lib, ptrs=tuple(ptrs)) == UNSUPPORTED
+    assert decode(lib, kbar=A + 4, nb=7) == UNSUPPORTED
+    assert decode(lib, sel=A + 8) == UNSUPPORTED

@@ -208,3 +208,63 @@ def test_streams(moba):
     s.synchronize()
     assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16))
     assert torch.equal(l, ref_l)
+
+
+# Decode step: (N, H, D, B, topk, seed). B dividing N or not (partial own
+# block), the first token, D = 64, the own block alone, topk above the number
+# of past blocks (full attention), many blocks with B = 64, B not a multiple
+# of the attention chunk.
+DECODE = [
+    (4096, 4, 128, 256, 3, 1),
+    (4000, 2, 128, 256, 3, 2),
+    (1, 2, 128, 64, 3, 3),
+    (777, 3, 64, 128, 2, 4),
+    (2048, 2, 128, 512, 1, 5),
+    (8192, 2, 128, 512, 100, 6),
+    (6000, 1, 128, 64, 9, 7),
+    (3333, 2, 128, 1000, 2, 8),
+    (32768, 8, 128, 512, 3, 9),
+]
+
+
+@pytest.mark.parametrize("case", DECODE, ids=lambda c: "N{}_H{}_D{}_B{}_k{}".format(*c[:5]))
+def test_decode_parity(moba, case):
+    from oracle import gate_scores, moba_decode_ref, pooled_keys_fp32
+    from tests.parity import TIE_REL
+    N, H, D, B, topk, seed = case
+    q, k, v = synth.make_qkv(N, H, D, seed=[300 + seed, 0], dtype="bf16")
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    qn = qd[N - 1].contiguous()
+    sel = torch.empty((H, topk), dtype=torch.int32, device="cuda")
+    out, lse = moba.decode(qn, kd, vd, B, topk, sel=sel)
+    j = (N - 1) // B
+    # The same call with the block means supplied (as a decode loop would keep them).
+    if j > 0:
+        # Exact fp64 means rounded once to fp32, as moba_block_mean_keys writes them
+        # (computed here with torch so that any block size works).
+        kbar = kd[:j * B].double().reshape(j, B, H, D).mean(dim=1).float().permute(1, 0, 2).contiguous()
+        out2, lse2 = moba.decode(qn, kd, vd, B, topk, kbar=kbar)
+    else:
+        out2, lse2 = moba.decode(qn, kd, vd, B, topk)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
+    gsel = sel.cpu().numpy()
+    _, _, rsel = moba_decode_ref(q[N - 1], k, v, B, topk)
+    exempt = 0
+    for h in range(H):
+        if np.array_equal(gsel[h], rsel[h]):
+            continue
+        # Near tie: the kept past blocks' fp32 scores agree within TIE_REL of the row's largest |score|.
+        g = gate_scores(q[N - 1, h][None, :], pooled_keys_fp32(k[:j * B], B)[h])[0].astype(np.float64)
+        a = sorted(g[[int(x) for x in rsel[h] if 0 <= x < j]])
+        b = sorted(g[[int(x) for x in gsel[h] if 0 <= x < j]])
+        assert list(gsel[h][gsel[h] >= 0]) == sorted(set(int(x) for x in gsel[h] if x >= 0)) and j in gsel[h]
+        assert len(a) == len(b) and np.all(np.abs(np.array(a) - np.array(b)) <= TIE_REL * np.max(np.abs(g[:j])))
+        exempt += 1
+    ro, rl, _ = moba_decode_ref(q[N - 1], k, v, B, topk, sel=gsel)
+    err_o = max_abs(out.float().cpu().numpy(), ro)
+    err_l = max_abs(lse.cpu().numpy(), rl)
+    log(f"  decode N={N} H={H} D={D} B={B} k={topk}: exempt {exempt}, max|out| err {err_o:.3e}, max|lse| err {err_l:.3e}")
+    assert err_o <= OUT_TOL["bf16"]
+    assert err_l <= LSE_TOL["bf16"]
