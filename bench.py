@@ -11,6 +11,12 @@ fraction of the bf16 MFMA peak, per-stage device times from HIP events the
 library records on its stream, the roofline of the dominant kernel (the
 past-block attention launch), and the fp64 oracle timed on the host on a
 sample of query rows.
+
+A ``decode`` object beside it times ``moba_decode_fwd`` for the newest token of
+the same K/V cache (block means kept from the prefill, as a generation loop
+keeps them): once gated with the workload's top-k and once with top-k above
+the block count (full attention over the whole cache). Decode reads 4*D bytes
+of keys and values per attended key and head, so it is priced against HBM.
 """
 
 from __future__ import annotations
@@ -84,6 +90,41 @@ def traffic_for(workload: str):
     return t.get("bytes_per_launch")
 
 
+def decode_bench(moba, w, qd, kd, vd, steps: int):
+    """Decode step for the token at position N - 1 of the cache: gated with the
+    workload's top-k and as full attention (top-k = number of blocks)."""
+    import torch
+    q_new = qd[w.N - 1].contiguous()
+    kbar = moba.block_mean_keys(kd, w.block_size)
+    out = torch.empty_like(q_new)
+    lse = torch.empty((w.H,), dtype=torch.float32, device=qd.device)
+    n_blocks = (w.N + w.block_size - 1) // w.block_size
+    j = (w.N - 1) // w.block_size
+    res = {}
+    for name, topk in (("moba", w.topk), ("full", n_blocks)):
+        kept = min(topk, j + 1)
+        keys = (kept - 1) * w.block_size + (w.N - j * w.block_size)
+        nbytes = w.H * keys * 4 * w.D
+        for _ in range(5):
+            moba.decode(q_new, kd, vd, w.block_size, topk, kbar=kbar, out=out, lse=lse)
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(steps):
+            moba.decode(q_new, kd, vd, w.block_size, topk, kbar=kbar, out=out, lse=lse)
+        stop.record()
+        torch.cuda.synchronize()
+        us = 1e3 * start.elapsed_time(stop) / steps
+        res[name] = {"top_k": topk, "kept_blocks": kept, "attended_keys": keys, "us_per_step": us,
+                     "kv_gbytes": nbytes / 1e9, "achieved_gbs": nbytes / (us * 1e-6) / 1e9,
+                     "frac_hbm": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+    res["speedup_vs_full"] = res["full"]["us_per_step"] / res["moba"]["us_per_step"]
+    res["timing"] = ("back-to-back calls through the Python binding between two HIP events on the stream; "
+                     "host launch overhead is included where it exceeds the kernels' time")
+    return res
+
+
 def cpu_baseline(w, q, k, v, gpu_out, gpu_lse, target_s: float):
     """The fp64 oracle as it stands, on a seeded sample of query rows."""
     import threadpoolctl
@@ -132,6 +173,8 @@ def main():
     ap.add_argument("--workload", default="h32")
     ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--decode", choices=("on", "off"), default="on",
+                    help="also time the decode step on the same cache")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run plain device copies of this size (HBM counter calibration)")
     args = ap.parse_args()
@@ -250,6 +293,12 @@ def main():
         },
         "device": info,
     }
+
+    if args.decode == "on":
+        result["decode"] = decode_bench(moba, w, qd, kd, vd, max(50, 10 * args.steps))
+        d = result["decode"]
+        print(f"[bench] decode: gated {d['moba']['us_per_step']:.1f} us, full {d['full']['us_per_step']:.1f} us "
+              f"({d['full']['achieved_gbs']:.0f} GB/s)", file=sys.stderr, flush=True)
 
     if args.cpu_baseline == "on":
         torch.cuda.synchronize()

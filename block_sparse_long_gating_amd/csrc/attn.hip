@@ -35,9 +35,6 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-// The running maximum is refreshed only when it grows by more than this many
-// powers of two.
-constexpr float kRescaleThreshold = 8.0f;
 
 template <typename T>
 struct AttnArgs {

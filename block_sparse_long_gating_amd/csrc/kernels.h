@@ -47,22 +47,25 @@ hipError_t launch_attention(const Problem& p, const void* q, const void* k, cons
 hipError_t launch_merge(const Problem& p, const Workspace& ws, void* out, float* lse, hipStream_t stream);
 
 // Decode step (bf16): the token at position N - 1 of a K/V cache.
-constexpr int kDecChunk = 256;   // keys per attention unit
+constexpr int kDecMaxChunk = 512;   // largest number of keys per attention unit
 struct DecodeArgs {
   const bf16* q;        // [H][D] query of the new token
   const bf16* k;        // [N][H][D] cache (the new token's key and value are the last rows)
   const bf16* v;
   const float* kbar;    // [H][kbar_blocks][D] fp32 means of the complete blocks (at least j of them)
   int kbar_blocks;
-  int32_t* sel;         // [H][S] kept blocks, ascending (own block last)
+  int32_t* sel;         // [H][S] kept blocks, ascending (own block last); unused when S == j + 1
   int32_t* sel_out;     // optional [H][topk] copy, -1 padded
-  float* scores;        // [H][j] gate scores
+  float* scores;        // [H][j] gate scores (used when j exceeds the LDS capacity)
   float* part_o;        // [H][units][D] unnormalised partial outputs
   float* part_ml;       // [H][units][2] partial (max, sum) in log2 units
   bf16* out;            // [H][D]
   float* lse;           // [H] natural log
   int64_t N;
-  int H, D, B, j, topk, S, chunks, units;
+  int H, D, B, j, topk, S;
+  int chunk;            // keys per unit (64 .. 512)
+  int chunks;           // units per kept block: ceil(B / chunk)
+  int units;            // S * chunks
   float scale_log2;     // log2(e) / sqrt(D)
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

@@ -286,10 +286,15 @@ int decode_impl(const void* q, const void* k, const void* v, const float* kbar, 
   a.j = static_cast<int>(j);
   a.topk = topk;
   a.S = static_cast<int>(std::min<int64_t>(topk, j + 1));
-  a.chunks = (B + moba::kDecChunk - 1) / moba::kDecChunk;
+  // Keys per unit: the largest of 512, 256, 128, 64 that still gives two units per CU.
+  a.chunk = moba::kDecMaxChunk;
+  while (a.chunk > 64 && static_cast<int64_t>(H) * a.S * ((B + a.chunk - 1) / a.chunk) < 2 * st->num_cus)
+    a.chunk /= 2;
+  a.chunks = (B + a.chunk - 1) / a.chunk;
+  if (static_cast<int64_t>(a.S) * a.chunks >= (int64_t{1} << 31)) return MOBA_ERR_UNSUPPORTED;
   a.units = a.S * a.chunks;
   a.scale_log2 = 1.4426950408889634f / std::sqrt(static_cast<float>(D));
-  const bool own_kbar = kbar == nullptr && j > 0;
+  const bool own_kbar = kbar == nullptr && topk < j + 1;   // block means only matter when the gate chooses
   Layout L;
   const size_t o_sel = L.add(static_cast<size_t>(H) * a.S * 4);
   const size_t o_sc = L.add(static_cast<size_t>(H) * j * 4);

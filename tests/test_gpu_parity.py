@@ -224,6 +224,7 @@ DECODE = [
     (6000, 1, 128, 64, 9, 7),
     (3333, 2, 128, 1000, 2, 8),
     (32768, 8, 128, 512, 3, 9),
+    (140000, 1, 64, 64, 4, 10),      # 2187 past blocks: gate scores outside LDS
 ]
 
 
