@@ -1,4 +1,4 @@
-"""fp64 CPU oracle of MoBA causal prefill and decode (test infrastructure only).
+"""fp64 CPU oracle of MoBA causal prefill (forward and backward) and decode (test infrastructure only).
 
 Only the tests, the package smoke check and the benchmark's CPU-baseline leg use
 this package. It shares no code with the HIP library and imports nothing from it.
@@ -8,6 +8,7 @@ from .moba_oracle import (  # noqa: F401
     attended_keys,
     attended_pairs_closed_form,
     gate_scores,
+    moba_backward_ref,
     moba_decode_ref,
     moba_ref,
     n_blocks,

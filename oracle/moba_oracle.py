@@ -43,6 +43,14 @@ Readings of points the pages leave open (each one is listed in the design notes)
 * The softmax scale is 1/√D; lse is the natural log of the sum of
   exp(q·k/√D) over A(t).
 
+``moba_backward_ref`` gives the gradients of the prefill output with respect
+to q, k and v for a given upstream gradient dO (the pages train and
+continually pretrain with MoBA: 智东西 section 三, the scaling-law and hybrid
+training experiments). The gate is a top-k choice, piecewise constant in q and
+k, so no gradient flows through it or through the block means: the selection
+is held fixed and the gradients are those of the masked softmax attention over
+A(t) (the textbook softmax Jacobian).
+
 ``moba_decode_ref`` is the generation step after the prefill: the newest token
 (position N - 1 of a cache whose length need not be a multiple of B, so its
 own block may be partial) gated and attended exactly like a prefill row; with
@@ -359,3 +367,114 @@ def moba_decode_ref(q_new, k, v, block_size: int, topk: int, kbar32=None, sel=No
         out[h] = p[0] @ v_att
         lse[h] = l[0]
     return out, lse, sel
+
+
+def _backward_dense(q, k, v, dout, block_size, sel, heads, dq, dk, dv, scale):
+    """Dense masked form, per (head, query block j): the logits of the block's
+    rows against every key of blocks 0..j, masked to A(t), softmax P, then
+    dV += Pᵀ dO, dP = dO Vᵀ, dL = P (dP - Σ_keys P dP), dQ = scale dL K,
+    dK += scale dLᵀ Q."""
+    N, H, D = q.shape
+    n = N // block_size
+    B = block_size
+    for oh, h in enumerate(heads):
+        for j in range(n):
+            t = np.arange(j * B, (j + 1) * B)
+            nk = (j + 1) * B
+            qh = np.asarray(q[t, h, :], np.float64)
+            doh = np.asarray(dout[t, h, :], np.float64)
+            kh = np.asarray(k[:nk, h, :], np.float64)
+            vh = np.asarray(v[:nk, h, :], np.float64)
+            chosen = np.zeros((B, n), dtype=bool)
+            for i, r in enumerate(t):
+                srow = sel[h, r]
+                chosen[i, srow[srow >= 0]] = True
+            key_pos = np.arange(nk)
+            mask = chosen[:, key_pos // B] & (key_pos[None, :] <= t[:, None])
+            logits = np.where(mask, (qh @ kh.T) * scale, -np.inf)
+            p, _ = _softmax_rows(logits)
+            dp = doh @ vh.T
+            dl = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+            dq[t, oh] = scale * (dl @ kh)
+            dk[:nk, oh] += scale * (dl.T @ qh)
+            dv[:nk, oh] += p.T @ doh
+
+
+def _backward_by_block(q, k, v, dout, block_size, sel, heads, dq, dk, dv, scale):
+    """The same gradients with the logits of each chosen block formed only for
+    the rows that chose it: a first pass gives every row's softmax maximum and
+    denominator over A(t), a second the row sums Σ_keys P dP, a third the
+    gradient terms of each block."""
+    N, H, D = q.shape
+    B = block_size
+    rows = np.arange(N)
+    jrow = rows // B
+    for oh, h in enumerate(heads):
+        qh = np.asarray(q[:, h, :], np.float64)
+        doh = np.asarray(dout[:, h, :], np.float64)
+        s = sel[h]
+        groups = []
+        for b in np.unique(s[s >= 0]):
+            ridx = np.nonzero((s == b).any(axis=1))[0]
+            groups.append((int(b), ridx, jrow[ridx] == b))
+
+        def probs_of(b, ridx, own, m, l):
+            kb = np.asarray(k[b * B:(b + 1) * B, h, :], np.float64)
+            lg = (qh[ridx] @ kb.T) * scale
+            if own.any():
+                kpos = b * B + np.arange(B)
+                lg[own] = np.where(kpos[None, :] <= ridx[own][:, None], lg[own], -np.inf)
+            if m is None:
+                return lg
+            return np.exp(lg - m[ridx][:, None]) / l[ridx][:, None]
+
+        m = np.full(N, -np.inf)
+        for b, ridx, own in groups:
+            m[ridx] = np.maximum(m[ridx], probs_of(b, ridx, own, None, None).max(axis=1))
+        l = np.zeros(N)
+        for b, ridx, own in groups:
+            l[ridx] += np.exp(probs_of(b, ridx, own, None, None) - m[ridx][:, None]).sum(axis=1)
+        delta = np.zeros(N)
+        for b, ridx, own in groups:
+            vb = np.asarray(v[b * B:(b + 1) * B, h, :], np.float64)
+            p = probs_of(b, ridx, own, m, l)
+            delta[ridx] += np.sum(p * (doh[ridx] @ vb.T), axis=1)
+        for b, ridx, own in groups:
+            kb = np.asarray(k[b * B:(b + 1) * B, h, :], np.float64)
+            vb = np.asarray(v[b * B:(b + 1) * B, h, :], np.float64)
+            p = probs_of(b, ridx, own, m, l)
+            dl = p * (doh[ridx] @ vb.T - delta[ridx][:, None])
+            dq[ridx, oh] += scale * (dl @ kb)
+            dk[b * B:(b + 1) * B, oh] += scale * (dl.T @ qh[ridx])
+            dv[b * B:(b + 1) * B, oh] += p.T @ doh[ridx]
+
+
+def moba_backward_ref(q, k, v, dout, block_size: int, topk: int, sel=None, heads=None, method: str = "dense"):
+    """fp64 gradients of the MoBA causal prefill output.
+
+    ``dout`` [N, H, D] is the upstream gradient of ``out``; the lse output
+    carries none. The selection (``sel`` [H, N, topk], default: the oracle's
+    own gate) is held fixed: the top-k choice has no gradient. ``heads``
+    limits the work to some heads (default: all). ``method`` is "dense" (the
+    masked form per query block) or "blocks" (the logits of each chosen block
+    for the rows that chose it).
+
+    Returns ``(dq, dk, dv, sel)``: gradients [N, len(heads), D] fp64.
+    """
+    q = np.asarray(q)
+    N, H, D = q.shape
+    n_blocks(N, block_size)
+    if sel is None:
+        sel, _ = select_blocks(q, k, block_size, topk)
+    heads = list(range(H)) if heads is None else [int(h) for h in heads]
+    softmax_scale = 1.0 / math.sqrt(D)
+    dq = np.zeros((N, len(heads), D), np.float64)
+    dk = np.zeros((N, len(heads), D), np.float64)
+    dv = np.zeros((N, len(heads), D), np.float64)
+    if method == "dense":
+        _backward_dense(q, k, v, dout, block_size, sel, heads, dq, dk, dv, softmax_scale)
+    elif method == "blocks":
+        _backward_by_block(q, k, v, dout, block_size, sel, heads, dq, dk, dv, softmax_scale)
+    else:
+        raise ValueError(method)
+    return dq, dk, dv, sel

@@ -433,10 +433,119 @@ def pin_decode_matches_prefill_row(m):
         assert np.array_equal(s2, sel) and np.array_equal(o2, out) and np.array_equal(l2, lse)
 
 
+# ---------------------------------------------------------------------------
+# backward pins
+# ---------------------------------------------------------------------------
+
+def _autograd_masked(q, k, v, dout, mask):
+    """dq, dk, dv of one head through torch autograd of SDPA (fp64) with a boolean mask."""
+    qh, kh, vh = (_t64(x).requires_grad_(True) for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(qh[None], kh[None], vh[None], attn_mask=mask[None])[0]
+    o.backward(_t64(dout))
+    return qh.grad.numpy(), kh.grad.numpy(), vh.grad.numpy()
+
+
+def _brute_mask(sel_h, N, B):
+    mask = torch.zeros((N, N), dtype=torch.bool)
+    for t in range(N):
+        chosen = set(int(x) for x in sel_h[t] if x >= 0)
+        for s in range(t + 1):
+            if s // B in chosen:
+                mask[t, s] = True
+    return mask
+
+
+def pin_backward_full_causal(m):
+    """top_k >= n: the gradients of plain causal attention (torch autograd of SDPA)."""
+    N, H, D, B = 64, 2, 8, 8
+    q, k, v = _rand(N, H, D, 51)
+    do = np.random.default_rng(52).standard_normal((N, H, D))
+    dq, dk, dv, _ = m.moba_backward_ref(q, k, v, do, B, N // B + 1)
+    causal = torch.ones(N, N, dtype=torch.bool).tril()
+    for h in range(H):
+        rq, rk, rv = _autograd_masked(q[:, h], k[:, h], v[:, h], do[:, h], causal)
+        for got, ref in ((dq, rq), (dk, rk), (dv, rv)):
+            assert np.allclose(got[:, h], ref, atol=1e-12, rtol=0)
+
+
+def pin_backward_block_diagonal(m):
+    """top_k = 1: the gradients of block-diagonal causal attention."""
+    N, H, D, B = 48, 1, 8, 16
+    q, k, v = _rand(N, H, D, 53)
+    do = np.random.default_rng(54).standard_normal((N, H, D))
+    dq, dk, dv, _ = m.moba_backward_ref(q, k, v, do, B, 1)
+    blockdiag = torch.tensor([[s // B == t // B and s <= t for s in range(N)] for t in range(N)])
+    rq, rk, rv = _autograd_masked(q[:, 0], k[:, 0], v[:, 0], do[:, 0], blockdiag)
+    for got, ref in ((dq, rq), (dk, rk), (dv, rv)):
+        assert np.allclose(got[:, 0], ref, atol=1e-12, rtol=0)
+
+
+def pin_backward_brute(m):
+    """Tiny inputs: autograd of SDPA under the mask of the exhaustive-search selection, both methods."""
+    for N, H, D, B, topk, seed in [(32, 2, 4, 4, 3, 55), (48, 1, 4, 8, 2, 56), (24, 2, 4, 2, 4, 57)]:
+        q, k, v = _rand(N, H, D, seed)
+        do = np.random.default_rng(seed + 100).standard_normal((N, H, D))
+        bsel = brute_selection(q, k, B, topk)
+        for method in ("dense", "blocks"):
+            dq, dk, dv, _ = m.moba_backward_ref(q, k, v, do, B, topk, method=method)
+            for h in range(H):
+                rq, rk, rv = _autograd_masked(q[:, h], k[:, h], v[:, h], do[:, h], _brute_mask(bsel[h], N, B))
+                for got, ref in ((dq, rq), (dk, rk), (dv, rv)):
+                    assert np.allclose(got[:, h], ref, atol=1e-12, rtol=0), (N, B, topk, method)
+
+
+def pin_backward_finite_difference(m):
+    """Directional derivatives of <dO, out> by central differences of the forward oracle
+    (selection held fixed), for q, k and v separately."""
+    N, H, D, B, topk = 64, 2, 8, 8, 3
+    q, k, v = (x.astype(np.float64) for x in _rand(N, H, D, 58))
+    rng = np.random.default_rng(59)
+    do = rng.standard_normal((N, H, D))
+    dq, dk, dv, sel = m.moba_backward_ref(q, k, v, do, B, topk)
+    eps = 1e-6
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        u = rng.standard_normal((N, H, D))
+        plus = [q, k, v]
+        minus = [q, k, v]
+        plus[which] = plus[which] + eps * u
+        minus[which] = minus[which] - eps * u
+        op, _, _ = m.moba_ref(*plus, B, topk, sel=sel)
+        om_, _, _ = m.moba_ref(*minus, B, topk, sel=sel)
+        fd = np.sum(do * (op - om_)) / (2 * eps)
+        an = np.sum(grad * u)
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (which, fd, an)
+
+
+def pin_backward_invariants(m):
+    """Softmax rows sum to one: Σ_keys dK = 0 and Σ_keys dV = Σ_queries dO, per head."""
+    N, H, D, B, topk = 128, 3, 8, 16, 3
+    q, k, v = _rand(N, H, D, 60)
+    do = np.random.default_rng(61).standard_normal((N, H, D))
+    for method in ("dense", "blocks"):
+        dq, dk, dv, _ = m.moba_backward_ref(q, k, v, do, B, topk, method=method)
+        assert np.allclose(dk.sum(axis=0), 0.0, atol=1e-11)
+        assert np.allclose(dv.sum(axis=0), do.sum(axis=0), atol=1e-11, rtol=0)
+
+
+def pin_backward_methods_agree(m):
+    """The dense and per-block evaluations agree, also on a subset of heads."""
+    N, H, D, B, topk = 256, 3, 16, 32, 3
+    q, k, v = _rand(N, H, D, 62)
+    do = np.random.default_rng(63).standard_normal((N, H, D))
+    a = m.moba_backward_ref(q, k, v, do, B, topk, heads=[2, 0])
+    b = m.moba_backward_ref(q, k, v, do, B, topk, heads=[2, 0], method="blocks")
+    full = m.moba_backward_ref(q, k, v, do, B, topk)
+    for x, y, z in zip(a[:3], b[:3], full[:3]):
+        assert np.allclose(x, y, atol=1e-12, rtol=0)
+        assert np.allclose(x, z[:, [2, 0]], atol=1e-12, rtol=0)
+
+
 ALL_PINS = [
     pin_bruteforce_tiny, pin_full_causal, pin_block_diagonal, pin_first_token, pin_constant_v,
     pin_zero_query, pin_invariants, pin_pages_worked_example, pin_pages_sparsity_table,
     pin_granularity, pin_closed_form_pairs, pin_lse_merge, pin_pooling_linearity,
     pin_gate_rounding, pin_row_mode_matches, pin_decode_full_attention, pin_decode_own_block,
     pin_decode_first_token, pin_decode_brute_selection, pin_decode_matches_prefill_row,
+    pin_backward_full_causal, pin_backward_block_diagonal, pin_backward_brute, pin_backward_finite_difference,
+    pin_backward_invariants, pin_backward_methods_agree,
 ]

@@ -28,11 +28,12 @@ def test_package_exports():
 MUTATIONS = {
     "no_forced_current_block": ("sorted(order[i, :topk - 1].tolist() + [int(j)])",
                                 "sorted(order[i, :topk].tolist())"),
-    "causal_mask_off_by_one": ("key_pos[None, :] <= t[:, None]", "key_pos[None, :] < t[:, None] + 2"),
+    "causal_mask_off_by_one": ("chosen[:, key_block] & (key_pos[None, :] <= t[:, None])",
+                               "chosen[:, key_block] & (key_pos[None, :] < t[:, None] + 2)"),
     "future_blocks_compete": ("neg[np.arange(n)[None, :] >= jj[:, None]] = np.inf",
                               "neg[np.arange(n)[None, :] > jj[:, None]] = np.inf"),
     "ascending_scores": ("neg = -sc.astype(np.float64)", "neg = sc.astype(np.float64)"),
-    "scale_1_over_d": ("scale = 1.0 / math.sqrt(D)", "scale = 1.0 / D"),
+    "scale_1_over_d": ("    scale = 1.0 / math.sqrt(D)\n    R = rows.shape[0]", "    scale = 1.0 / D\n    R = rows.shape[0]"),
     "pool_sum_not_mean": ("return np.ascontiguousarray((total / block_size).transpose(1, 0, 2))",
                           "return np.ascontiguousarray(total.transpose(1, 0, 2))"),
     "pool_wrong_axis": ("total += k64[:, r]", "total += k64[:, r][:, ::-1]"),
@@ -61,6 +62,17 @@ MUTATIONS = {
     "decode_wrong_query_head": ("logits = (k_att @ np.asarray(q_new[h], np.float64)) * inv_sqrt_d",
                                 "logits = (k_att @ np.asarray(q_new[(h + 1) % H], np.float64)) * inv_sqrt_d"),
     "decode_scale_1_over_d": ("inv_sqrt_d = 1.0 / math.sqrt(D)", "inv_sqrt_d = 1.0 / D"),
+    "backward_scale_1_over_d": ("softmax_scale = 1.0 / math.sqrt(D)", "softmax_scale = 1.0 / D"),
+    "backward_drops_row_sum": ("dl = p * (dp - np.sum(p * dp, axis=1, keepdims=True))", "dl = p * dp"),
+    "backward_dk_unscaled": ("dk[:nk, oh] += scale * (dl.T @ qh)", "dk[:nk, oh] += dl.T @ qh"),
+    "backward_dq_against_v": ("dq[t, oh] = scale * (dl @ kh)", "dq[t, oh] = scale * (dl @ vh)"),
+    "backward_dv_uses_logit_grad": ("dv[:nk, oh] += p.T @ doh", "dv[:nk, oh] += dl.T @ doh"),
+    "backward_mask_off_by_one": ("mask = chosen[:, key_pos // B] & (key_pos[None, :] <= t[:, None])",
+                                 "mask = chosen[:, key_pos // B] & (key_pos[None, :] < t[:, None])"),
+    "backward_blocks_delta_last_block_only": ("delta[ridx] += np.sum(p * (doh[ridx] @ vb.T), axis=1)",
+                                              "delta[ridx] = np.sum(p * (doh[ridx] @ vb.T), axis=1)"),
+    "backward_blocks_dk_from_dout": ("dk[b * B:(b + 1) * B, oh] += scale * (dl.T @ qh[ridx])",
+                                     "dk[b * B:(b + 1) * B, oh] += scale * (dl.T @ doh[ridx])"),
 }
 
 
