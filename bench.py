@@ -12,7 +12,9 @@ library records on its stream, the roofline of the dominant kernel (the
 past-block attention launch), and the fp64 oracle timed on the host on a
 sample of query rows.
 
-A ``decode`` object beside it times ``moba_decode_fwd`` for the newest token of
+A ``backward`` object times ``moba_prefill_bwd`` (dQ, dK, dV for a seeded
+upstream gradient) on the same inputs, effective TFLOP/s counted as 2.5x the
+forward's attended-pair work. A ``decode`` object beside it times ``moba_decode_fwd`` for the newest token of
 the same K/V cache (block means kept from the prefill, as a generation loop
 keeps them): once gated with the workload's top-k and once with top-k above
 the block count (full attention over the whole cache). Decode reads 4*D bytes
@@ -125,6 +127,32 @@ def decode_bench(moba, w, qd, kd, vd, steps: int):
     return res
 
 
+def backward_bench(moba, w, qd, kd, vd, out, lse, steps: int, warmup: int):
+    """moba_prefill_bwd on the same workload (upstream gradient: seeded N(0, 1))."""
+    import torch
+    from block_sparse_long_gating_amd import synth
+    do = torch.from_numpy(synth.bf16_bits(synth.make_grad(w.N, w.H, w.D, seed=[402, 9]))).view(torch.bfloat16)
+    do = do.to(qd.device)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(qd), torch.empty_like(qd)
+    for _ in range(warmup):
+        moba.prefill_backward(qd, kd, vd, out, lse, do, w.block_size, w.topk, dq=dq, dk=dk, dv=dv)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        moba.prefill_backward(qd, kd, vd, out, lse, do, w.block_size, w.topk, dq=dq, dk=dk, dv=dv)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    # FlashAttention convention: the backward of an attended pair is 2.5x its
+    # forward work (S, dP, dV, dQ, dK: five D-long products, 10 D FLOPs).
+    flops = 10.0 * w.D * effective_pairs(w.N, w.block_size, w.topk) * w.H
+    return {"ms_per_step": ms, "effective_gflop": flops / 1e9, "effective_tflops": flops / (ms * 1e-3) / 1e12,
+            "pct_peak": 100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "includes": "block mean-pool, gate, query lists (recomputed), delta, dK/dV, dQ"}
+
+
 def cpu_baseline(w, q, k, v, gpu_out, gpu_lse, target_s: float):
     """The fp64 oracle as it stands, on a seeded sample of query rows."""
     import threadpoolctl
@@ -173,6 +201,8 @@ def main():
     ap.add_argument("--workload", default="h32")
     ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--backward", choices=("on", "off"), default="on",
+                    help="also time the backward pass on the same workload")
     ap.add_argument("--decode", choices=("on", "off"), default="on",
                     help="also time the decode step on the same cache")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -293,6 +323,12 @@ def main():
         },
         "device": info,
     }
+
+    if args.backward == "on":
+        result["backward"] = backward_bench(moba, w, qd, kd, vd, out, lse, args.steps, args.warmup)
+        bw = result["backward"]
+        print(f"[bench] backward: {bw['ms_per_step']:.3f} ms/step, {bw['effective_tflops']:.1f} effective TFLOP/s",
+              file=sys.stderr, flush=True)
 
     if args.decode == "on":
         result["decode"] = decode_bench(moba, w, qd, kd, vd, max(50, 10 * args.steps))

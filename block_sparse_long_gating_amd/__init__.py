@@ -39,6 +39,7 @@ _SIGNATURES = {
     "moba_prefill_fwd_f32": [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P],
     "moba_prefill_fwd_timed": [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P],
     "moba_decode_fwd": [_P, _P, _P, _P, _I32, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P],
+    "moba_prefill_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P],
     "moba_status_string": [ctypes.c_int],
     "moba_last_hip_error": [],
 }
@@ -205,6 +206,32 @@ def prefill(q, k, v, block_size: int, topk: int, out=None, lse=None, events: "St
     _check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), N, H, D, block_size, topk,
               _stream(q.device)), "moba_prefill_fwd")
     return out, lse
+
+
+def prefill_backward(q, k, v, out, lse, dout, block_size: int, topk: int, dq=None, dk=None, dv=None):
+    """Gradients of the bf16 MoBA prefill output: returns ``(dq, dk, dv)`` [N, H, D] bf16.
+
+    ``out`` and ``lse`` are what :func:`prefill` returned for the same inputs;
+    ``dout`` is the upstream gradient of ``out``. The top-k selection carries
+    no gradient (it is recomputed and held fixed)."""
+    import torch
+    N, H, D, f32 = _check_qkv(q, k, v, out, dout)
+    if f32:
+        raise TypeError("the backward pass takes bf16 tensors")
+    if lse.shape != (H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous fp32 [H, N] tensor on q's device")
+    grads = []
+    for g in (dq, dk, dv):
+        if g is None:
+            g = torch.empty_like(q)
+        elif g.shape != q.shape or g.dtype != q.dtype or not g.is_contiguous() or g.device != q.device:
+            raise ValueError("dq, dk, dv must be contiguous tensors like q")
+        grads.append(g)
+    lib = load_library()
+    _check(lib.moba_prefill_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                dout.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(),
+                                N, H, D, block_size, topk, _stream(q.device)), "moba_prefill_bwd")
+    return tuple(grads)
 
 
 def decode(q_new, k, v, block_size: int, topk: int, kbar=None, out=None, lse=None, sel=None):

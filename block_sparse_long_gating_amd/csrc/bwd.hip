@@ -1,0 +1,494 @@
+// Backward pass of the MoBA causal prefill (bf16): dQ, dK, dV of the output.
+//
+// The pages train and continually pretrain with MoBA (智东西 report, section
+// 三); the gate is a top-k choice with no gradient, so the selection of the
+// forward pass is recomputed and held fixed, and the gradients are those of
+// the block-sparse softmax attention (P the probabilities over the attended
+// keys, dO the upstream gradient):
+//   dV = Pᵀ dO,  dP = dO Vᵀ,  dS = P ⊙ (dP − Δ) with Δ_t = Σ_d dO_t O_t,
+//   dQ = dS K / √D,  dK = dSᵀ Q / √D.
+// P is rebuilt from the scores and the forward's log-sum-exp.
+//
+// Kernels (v_mfma_f32_32x32x16_bf16 for every product; C layout: lane l holds
+// column l % 32 and rows 8 (r / 4) + 4 (l / 32) + r % 4 of accumulator
+// element r; the 16-row groups that feed a second product are taken in that
+// same row order, through the LDS transpose read where the operand is
+// row-major in LDS):
+//   bwd_delta_kernel   Δ per (head, query): D/8 lanes per row.
+//   bwd_dkdv_kernel    key-stationary: one workgroup per (head, key block,
+//                      128-key chunk) walks every query that attends the
+//                      chunk: the block's query list (past selections) and
+//                      the block's own later queries (causal mask), in
+//                      64-query tiles staged in LDS (double-buffered through
+//                      registers, list entries looked up a tile ahead). Eight
+//                      waves: wave w holds K and V of key group w % 4 (32
+//                      keys) in registers and computes, for query half w / 4,
+//                        S = Q Kᵀ, dP = dO Vᵀ (queries on the rows), P, dS,
+//                      which go to LDS as bf16; then for dims half w / 4 and
+//                      the whole tile
+//                        dVᵀ += dOᵀ P, dKᵀ += Qᵀ dS (dOᵀ, Qᵀ by transpose reads).
+//                      Each key is owned by one workgroup: no atomics.
+//   bwd_dq_kernel      query-stationary over the same work items as the
+//                      forward pass (a block and up to 256 of its queries;
+//                      eight waves of 32 queries with Q and dO in registers),
+//                      walking the block's 64-key tiles in LDS:
+//                        Sᵀ = K Qᵀ, dPᵀ = V dOᵀ (keys on the rows),
+//                        dQᵀ += Kᵀ dSᵀ (Kᵀ by transpose reads).
+//                      Past-block items write fp32 partial rows in list
+//                      order; the own-block items run afterwards, add the
+//                      query's past partials (list positions from the scatter)
+//                      and write dQ.
+#include "common.h"
+#include "kernels.h"
+
+namespace moba {
+
+namespace {
+
+typedef short s16x4b __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4b lds_s16x4b;
+
+constexpr float kBwdLog2e = 1.4426950408889634f;
+constexpr int kBwdQTile = 64;      // queries per LDS tile of the dK/dV kernel
+constexpr int kBwdKeys = 128;      // keys per dK/dV workgroup (4 waves x 32)
+constexpr int kBwdKTile = 64;      // keys per LDS tile of the dQ kernel
+
+template <int D>
+struct BwdLay {
+  static constexpr int kRow = 2 * D + 16;          // padded LDS row (bytes)
+  static constexpr int kTile = 64 * kRow;          // one 64-row tile
+  static constexpr int kChunks = D / 8;            // 16-byte chunks per row
+};
+
+// MFMA over D: rows from a row-major LDS tile (A operand, per-lane pointer to
+// row l % 32 at byte 16 (l / 32)), columns from registers (B operand).
+template <int D>
+__device__ __forceinline__ f32x16 rows_by_regs(const char* ap, const bf16x8 (&b)[D / 16]) {
+  f32x16 s;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ap + 32 * c));
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[c], s, 0, 0, 0);
+  }
+  return s;
+}
+
+// A operand "columns of a row-major LDS tile as rows": for a 16-row group
+// starting at `p` (already offset by the lane's transpose-read position) and
+// 32 columns starting at column 32 dc, the 8 rows the C layout pairs with this
+// lane (4 (l / 32) + 0..3, then 8 + 4 (l / 32) + 0..3).
+template <int kRow>
+__device__ __forceinline__ bf16x8 tr_operand(const char* p) {
+  const s16x4b lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4b*)(p));
+  const s16x4b hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4b*)(p + 8 * kRow));
+  const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo);
+  const bf16x4 h4 = __builtin_bit_cast(bf16x4, hi);
+  return bf16x8{l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
+}
+
+__device__ __forceinline__ void pack16(const f32x16& x, bf16x8 (&p)[2]) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) p[r >> 3][r & 7] = static_cast<bf16>(x[r]);
+}
+
+__device__ __forceinline__ uint4 ld16(const bf16* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
+  const int kl = a.D / 8;                          // lanes per row
+  const int rows = 256 / kl;
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * rows + threadIdx.x / kl;   // g = t * H + h
+  const int li = threadIdx.x % kl;
+  float s = 0.f;
+  if (g < a.N * a.H) {
+    const bf16x8 o8 = __builtin_bit_cast(bf16x8, ld16(a.out + g * a.D + 8 * li));
+    const bf16x8 d8 = __builtin_bit_cast(bf16x8, ld16(a.dout + g * a.D + 8 * li));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = fmaf(static_cast<float>(o8[e]), static_cast<float>(d8[e]), s);
+  }
+  for (int w = 1; w < kl; w <<= 1) s += __shfl_xor(s, w);
+  if (g < a.N * a.H && li == 0) {
+    const int64_t t = g / a.H;
+    const int h = static_cast<int>(g % a.H);
+    a.delta[static_cast<int64_t>(h) * a.N + t] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV
+// ---------------------------------------------------------------------------
+
+// Eight waves over 128 keys: wave w computes S and dP for key group kg = w % 4
+// (32 keys, K and V in registers) and query half w / 4 of each 64-query tile,
+// hands P and dS to the workgroup through LDS, then accumulates dKᵀ and dVᵀ
+// for key group kg and dims half w / 4 over the whole tile.
+template <int D>
+__global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
+  using L = BwdLay<D>;
+  constexpr int kXRow = 2 * kBwdQTile + 16;        // P / dS exchange row (one key, 64 queries, bf16)
+  constexpr int kX = 32 * kXRow;                   // one key group
+  constexpr int kDH = D / 2;                       // dims accumulated per wave
+  __shared__ __align__(16) char tiles[2][2 * L::kTile];   // [buffer][Q tile, dO tile]
+  __shared__ __align__(16) char xch[2][4 * kX];            // [P, dS][key group]
+  __shared__ __align__(16) float s_lse[2][kBwdQTile];
+  __shared__ __align__(16) float s_del[2][kBwdQTile];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int kg = w & 3, wh = w >> 2;               // key group; query half (S, dP) and dims half (dK, dV)
+  const int chunks = (a.B + kBwdKeys - 1) / kBwdKeys;
+  // XCD-aware order: the chunks of one (head, block) run on one XCD at the same
+  // time (they read the same query rows), consecutive (head, block) pairs go
+  // round-robin over the XCDs, and blocks are taken in ascending order (their
+  // query lists get shorter).
+  const int G = static_cast<int>(gridDim.x);
+  int li = static_cast<int>(blockIdx.x);
+  if (G % (kXcds * chunks) == 0) {
+    const int xcd = li % kXcds, slot = li / kXcds;
+    li = ((slot / chunks) * kXcds + xcd) * chunks + slot % chunks;
+  }
+  const int c = li % chunks;
+  const int rest = li / chunks;
+  const int h = rest % a.H, b = rest / a.H;
+  const int kofs = kBwdKeys * c + 32 * kg;         // this wave's first key inside the block
+  const bool active = kofs < a.B;
+  const int64_t key0 = static_cast<int64_t>(b) * a.B + kofs;
+  const int64_t hb = static_cast<int64_t>(h) * a.n + b;
+  const int lstart = a.offs[hb], llen = a.totals[hb];
+  const int own0 = kBwdKeys * c;                   // first own query (offset in the block) that sees the chunk
+  const int t_past = (llen + kBwdQTile - 1) / kBwdQTile;
+  const int t_all = t_past + (a.B - own0 + kBwdQTile - 1) / kBwdQTile;
+  const int64_t hd = static_cast<int64_t>(h) * D;
+  const int64_t row_el = static_cast<int64_t>(a.H) * D;
+
+  bf16x8 kr[D / 16], vr[D / 16];
+  {
+    const int64_t kk = active ? key0 + col : 0;
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc) {
+      kr[cc] = __builtin_bit_cast(bf16x8, ld16(a.k + kk * row_el + hd + 16 * cc + 8 * half));
+      vr[cc] = __builtin_bit_cast(bf16x8, ld16(a.v + kk * row_el + hd + 16 * cc + 8 * half));
+    }
+  }
+  f32x16 adv[kDH / 32], adk[kDH / 32];
+#pragma unroll
+  for (int dc = 0; dc < kDH / 32; ++dc)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) adv[dc][r] = adk[dc][r] = 0.f;
+
+  // Tile rows: the token of row r of tile i (-1: no query).
+  auto token = [&](int i, int r) -> int64_t {
+    if (i >= t_all) return -1;
+    if (i < t_past) {
+      const int e = kBwdQTile * i + r;
+      return e < llen ? a.qidx[lstart + e] : -1;
+    }
+    const int o = own0 + kBwdQTile * (i - t_past) + r;
+    return o < a.B ? static_cast<int64_t>(b) * a.B + o : -1;
+  };
+  // Loader: 64 rows x kChunks 16-byte chunks of Q and dO; the rows' tokens are
+  // looked up one tile ahead of the row loads.
+  constexpr int kPer = kBwdQTile * L::kChunks / 512;
+  uint4 pq[kPer], pd[kPer];
+  int64_t tok[kPer];
+  int64_t tok_l = -1;
+  float plse = INFINITY, pdel = 0.f;
+  auto lookup = [&](int i) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) tok[u] = token(i, (tid + 512 * u) / L::kChunks);
+    if (tid < kBwdQTile) tok_l = token(i, tid);
+  };
+  auto fetch = [&]() {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int ch = (tid + 512 * u) % L::kChunks;
+      const bool ok = tok[u] >= 0;
+      const int64_t off = (ok ? tok[u] : 0) * row_el + hd + 8 * ch;
+      pq[u] = ok ? ld16(a.q + off) : make_uint4(0, 0, 0, 0);
+      pd[u] = ok ? ld16(a.dout + off) : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < kBwdQTile) {
+      const bool ok = tok_l >= 0;
+      plse = ok ? a.lse[static_cast<int64_t>(h) * a.N + tok_l] * kBwdLog2e : INFINITY;
+      pdel = ok ? a.delta[static_cast<int64_t>(h) * a.N + tok_l] : 0.f;
+    }
+  };
+  auto commit = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int idx = tid + 512 * u;
+      const int r = idx / L::kChunks, ch = idx % L::kChunks;
+      *reinterpret_cast<uint4*>(&tiles[buf][r * L::kRow + 16 * ch]) = pq[u];
+      *reinterpret_cast<uint4*>(&tiles[buf][L::kTile + r * L::kRow + 16 * ch]) = pd[u];
+    }
+    if (tid < kBwdQTile) {
+      s_lse[buf][tid] = plse;
+      s_del[buf][tid] = pdel;
+    }
+  };
+
+  const int tg = lane >> 4, te = (lane >> 2) & 3, tq = lane & 3;
+  const int row_lane = col * L::kRow + 16 * half;
+  const int tr_lane = (4 * (tg >> 1) + te) * L::kRow + 2 * (16 * (tg & 1) + 4 * tq);
+  char* xp = xch[0] + kg * kX + col * kXRow;       // this lane's key row of P (dS: xch[1])
+  lookup(0);
+  fetch();
+  commit(0);
+  lookup(1);
+  __syncthreads();
+  for (int i = 0; i < t_all; ++i) {
+    const int buf = i & 1;
+    if (i + 1 < t_all) {
+      fetch();          // rows of tile i + 1 (tokens looked up last iteration)
+      lookup(i + 2);
+    }
+    const char* qt = tiles[buf];
+    const char* dt = tiles[buf] + L::kTile;
+    if (active) {
+      // S and dP for key group kg and queries 32 wh .. 32 wh + 31 of the tile.
+      const bool own = i >= t_past;
+      const int q0 = own0 + kBwdQTile * (i - t_past);   // own tiles: offset of the tile's first query
+      const f32x16 s = rows_by_regs<D>(qt + wh * 32 * L::kRow + row_lane, kr);
+      const f32x16 dp = rows_by_regs<D>(dt + wh * 32 * L::kRow + row_lane, vr);
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int rq = wh * 32 + 8 * g4 + 4 * half;
+        const float4 l4 = *reinterpret_cast<const float4*>(&s_lse[buf][rq]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&s_del[buf][rq]);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+        bf16x4 p4, ds4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g4 + e;
+          float pr = __builtin_amdgcn_exp2f(fmaf(s[r], a.scale_log2, -lv[e]));
+          if (own && kofs + col > q0 + rq + e) pr = 0.f;   // key after the query
+          p4[e] = static_cast<bf16>(pr);
+          ds4[e] = static_cast<bf16>(pr * (dp[r] - dv[e]));
+        }
+        *reinterpret_cast<bf16x4*>(xp + 2 * rq) = p4;
+        *reinterpret_cast<bf16x4*>(xp + 4 * kX + 2 * rq) = ds4;
+      }
+    }
+    __syncthreads();
+    if (active) {
+      // dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS for dims kDH wh .. and the whole tile.
+#pragma unroll
+      for (int g = 0; g < kBwdQTile / 16; ++g) {
+        const int q16 = 16 * g + 4 * half;
+        const bf16x4 pa = *reinterpret_cast<const bf16x4*>(xp + 2 * q16);
+        const bf16x4 pb = *reinterpret_cast<const bf16x4*>(xp + 2 * (q16 + 8));
+        const bf16x4 sa = *reinterpret_cast<const bf16x4*>(xp + 4 * kX + 2 * q16);
+        const bf16x4 sb = *reinterpret_cast<const bf16x4*>(xp + 4 * kX + 2 * (q16 + 8));
+        const bf16x8 pp = bf16x8{pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
+        const bf16x8 dsp = bf16x8{sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+        const int roff = 16 * g * L::kRow + tr_lane + 2 * kDH * wh;
+#pragma unroll
+        for (int dc = 0; dc < kDH / 32; ++dc) {
+          const bf16x8 dot = tr_operand<L::kRow>(dt + roff + 64 * dc);
+          adv[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot, pp, adv[dc], 0, 0, 0);
+          const bf16x8 qtr = tr_operand<L::kRow>(qt + roff + 64 * dc);
+          adk[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qtr, dsp, adk[dc], 0, 0, 0);
+        }
+      }
+    }
+    if (i + 1 < t_all) commit(buf ^ 1);
+    __syncthreads();
+  }
+  if (!active) return;
+  // dKᵀ / dVᵀ rows are dims kDH wh + 32 dc + 8 g4 + 4 half + 0..3 of this lane's key.
+  const int64_t base = (key0 + col) * row_el + hd;
+#pragma unroll
+  for (int dc = 0; dc < kDH / 32; ++dc)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d0 = kDH * wh + 32 * dc + 8 * g4 + 4 * half;
+      bf16x4 kv4, vv4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kv4[e] = static_cast<bf16>(adk[dc][4 * g4 + e] * a.scale);
+        vv4[e] = static_cast<bf16>(adv[dc][4 * g4 + e]);
+      }
+      *reinterpret_cast<bf16x4*>(a.dk + base + d0) = kv4;
+      *reinterpret_cast<bf16x4*>(a.dv + base + d0) = vv4;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ
+// ---------------------------------------------------------------------------
+
+template <int D, bool kOwn>
+__global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
+  using L = BwdLay<D>;
+  __shared__ __align__(16) char tiles[2][2 * L::kTile];   // [buffer][K tile, V tile]
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  int h, b, count;
+  int64_t t0 = 0;         // own items: first query
+  int lstart = 0;         // past items: first list position
+  if (kOwn) {
+    const int per = (a.B + kAttnTile - 1) / kAttnTile;
+    const int x = blockIdx.x % per;
+    const int rest = blockIdx.x / per;
+    h = rest % a.H;
+    b = rest / a.H;
+    t0 = static_cast<int64_t>(b) * a.B + static_cast<int64_t>(x) * kAttnTile;
+    count = min(kAttnTile, a.B - x * kAttnTile);
+  } else {
+    if (static_cast<int>(blockIdx.x) >= a.counters[0]) return;
+    const WorkItem it = a.items[blockIdx.x];
+    h = it.h;
+    b = it.b;
+    lstart = it.start;
+    count = it.count;
+  }
+  const int64_t hd = static_cast<int64_t>(h) * D;
+  const int64_t row_el = static_cast<int64_t>(a.H) * D;
+  const int pos = 32 * w + col;                    // this lane's query inside the item
+  const bool valid = pos < count;
+  int64_t t = 0;
+  if (valid) t = kOwn ? t0 + pos : a.qidx[lstart + pos];
+  bf16x8 qr[D / 16], dr[D / 16];
+#pragma unroll
+  for (int cc = 0; cc < D / 16; ++cc) {
+    const int64_t off = t * row_el + hd + 16 * cc + 8 * half;
+    qr[cc] = valid ? __builtin_bit_cast(bf16x8, ld16(a.q + off)) : bf16x8{};
+    dr[cc] = valid ? __builtin_bit_cast(bf16x8, ld16(a.dout + off)) : bf16x8{};
+  }
+  const float lse2 = valid ? a.lse[static_cast<int64_t>(h) * a.N + t] * kBwdLog2e : INFINITY;
+  const float del = valid ? a.delta[static_cast<int64_t>(h) * a.N + t] : 0.f;
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int dc = 0; dc < D / 32; ++dc)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[dc][r] = 0.f;
+
+  // Key tiles of block b; the own block stops at the item's last query.
+  const int64_t kb0 = static_cast<int64_t>(b) * a.B;
+  const int nkeys = kOwn ? static_cast<int>(t0 - kb0) + count : a.B;
+  const int ntiles = (nkeys + kBwdKTile - 1) / kBwdKTile;
+  constexpr int kPer = kBwdKTile * L::kChunks / 512;
+  uint4 pk[kPer], pv[kPer];
+  auto fetch = [&](int i) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int idx = tid + 512 * u;
+      const int r = idx / L::kChunks, ch = idx % L::kChunks;
+      const int64_t off = (kb0 + kBwdKTile * i + r) * row_el + hd + 8 * ch;   // always inside block b
+      pk[u] = ld16(a.k + off);
+      pv[u] = ld16(a.v + off);
+    }
+  };
+  auto commit = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int idx = tid + 512 * u;
+      const int r = idx / L::kChunks, ch = idx % L::kChunks;
+      *reinterpret_cast<uint4*>(&tiles[buf][r * L::kRow + 16 * ch]) = pk[u];
+      *reinterpret_cast<uint4*>(&tiles[buf][L::kTile + r * L::kRow + 16 * ch]) = pv[u];
+    }
+  };
+  const int tg = lane >> 4, te = (lane >> 2) & 3, tq = lane & 3;
+  const int row_lane = col * L::kRow + 16 * half;
+  const int tr_lane = (4 * (tg >> 1) + te) * L::kRow + 2 * (16 * (tg & 1) + 4 * tq);
+  fetch(0);
+  commit(0);
+  __syncthreads();
+  for (int i = 0; i < ntiles; ++i) {
+    const int buf = i & 1;
+    if (i + 1 < ntiles) fetch(i + 1);
+    const char* kt = tiles[buf];
+    const char* vt = tiles[buf] + L::kTile;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const f32x16 s = rows_by_regs<D>(kt + kh * 32 * L::kRow + row_lane, qr);
+      const f32x16 dp = rows_by_regs<D>(vt + kh * 32 * L::kRow + row_lane, dr);
+      f32x16 ds;
+      const int64_t kbase = kb0 + kBwdKTile * i + 32 * kh;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = __builtin_amdgcn_exp2f(fmaf(s[r], a.scale_log2, -lse2));
+        if (kOwn && kbase + 8 * (r >> 2) + 4 * half + (r & 3) > t) pr = 0.f;   // key after the query
+        ds[r] = pr * (dp[r] - del);
+      }
+      bf16x8 dsp[2];
+      pack16(ds, dsp);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int roff = (kh * 32 + 16 * g) * L::kRow + tr_lane;
+#pragma unroll
+        for (int dc = 0; dc < D / 32; ++dc) {
+          const bf16x8 ktr = tr_operand<L::kRow>(kt + roff + 64 * dc);
+          acc[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktr, dsp[g], acc[dc], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+    if (i + 1 < ntiles) {
+      commit(buf ^ 1);
+      __syncthreads();
+    }
+  }
+  if (!valid) return;
+  // dQᵀ rows are dims 32 dc + 8 g4 + 4 half + 0..3 of this lane's query.
+  if (!kOwn) {
+    float* dst = a.part_dq + static_cast<int64_t>(lstart + pos) * D;
+#pragma unroll
+    for (int dc = 0; dc < D / 32; ++dc)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<float4*>(dst + 32 * dc + 8 * g4 + 4 * half) =
+            make_float4(acc[dc][4 * g4], acc[dc][4 * g4 + 1], acc[dc][4 * g4 + 2], acc[dc][4 * g4 + 3]);
+    return;
+  }
+  // Own block: add the query's past partials, scale, write dQ.
+  const int j = b;
+  const int np = min(j, a.topk - 1);
+  const int64_t ibase = (static_cast<int64_t>(h) * a.N + t) * a.lmax;
+  for (int s2 = 0; s2 < np; ++s2) {
+    const float* src = a.part_dq + static_cast<int64_t>(a.inv[ibase + s2]) * D;
+#pragma unroll
+    for (int dc = 0; dc < D / 32; ++dc)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const float4 x = *reinterpret_cast<const float4*>(src + 32 * dc + 8 * g4 + 4 * half);
+        acc[dc][4 * g4] += x.x;
+        acc[dc][4 * g4 + 1] += x.y;
+        acc[dc][4 * g4 + 2] += x.z;
+        acc[dc][4 * g4 + 3] += x.w;
+      }
+  }
+  bf16* dq = a.dq + t * row_el + hd;
+#pragma unroll
+  for (int dc = 0; dc < D / 32; ++dc)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      bf16x4 v4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v4[e] = static_cast<bf16>(acc[dc][4 * g4 + e] * a.scale);
+      *reinterpret_cast<bf16x4*>(dq + 32 * dc + 8 * g4 + 4 * half) = v4;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
+  const int64_t rows = a.N * a.H;
+  const int per = 256 / (a.D / 8);
+  bwd_delta_kernel<<<static_cast<unsigned>((rows + per - 1) / per), 256, 0, stream>>>(a);
+  const unsigned kv_grid = static_cast<unsigned>(static_cast<int64_t>(a.n) * a.H * ((a.B + kBwdKeys - 1) / kBwdKeys));
+  const unsigned own_grid = static_cast<unsigned>(static_cast<int64_t>(a.n) * a.H * ((a.B + kAttnTile - 1) / kAttnTile));
+  if (a.D == 128) {
+    bwd_dkdv_kernel<128><<<kv_grid, 512, 0, stream>>>(a);
+    if (a.max_items > 0) bwd_dq_kernel<128, false><<<static_cast<unsigned>(a.max_items), 512, 0, stream>>>(a);
+    bwd_dq_kernel<128, true><<<own_grid, 512, 0, stream>>>(a);
+  } else {
+    bwd_dkdv_kernel<64><<<kv_grid, 512, 0, stream>>>(a);
+    if (a.max_items > 0) bwd_dq_kernel<64, false><<<static_cast<unsigned>(a.max_items), 512, 0, stream>>>(a);
+    bwd_dq_kernel<64, true><<<own_grid, 512, 0, stream>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moba

@@ -70,4 +70,32 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+// Backward pass of the bf16 prefill: dQ, dK, dV of the output (the selection
+// and the query lists come from the gate and list stages of the same call).
+struct BwdArgs {
+  const bf16* q;        // [N][H][D]
+  const bf16* k;
+  const bf16* v;
+  const bf16* out;      // forward output [N][H][D]
+  const bf16* dout;     // upstream gradient of out [N][H][D]
+  const float* lse;     // forward log-sum-exp [H][N], natural log
+  bf16* dq;             // [N][H][D]
+  bf16* dk;
+  bf16* dv;
+  float* delta;         // [H][N] workspace: sum over d of dout * out
+  float* part_dq;       // [P_off][D] workspace: past-block dQ partials in list order (unscaled)
+  const int32_t* qidx;  // list entries (token of every (query, past block) pair)
+  const int32_t* offs;  // [H*n] list starts
+  const int32_t* totals;  // [H*n] list lengths
+  const int32_t* inv;   // [H][N][lmax] list position of each past selection
+  const WorkItem* items;  // past-block work items (count in counters[0])
+  const int32_t* counters;
+  int64_t N;
+  int H, D, B, n, topk, lmax;
+  int64_t max_items;
+  float scale;          // 1 / sqrt(D)
+  float scale_log2;     // log2(e) / sqrt(D)
+};
+hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
+
 }  // namespace moba

@@ -123,11 +123,13 @@ struct Layout {
 // Workspace offsets for the requested stages.
 struct WsPlan {
   size_t kbar, kpieces, cnt, totals, offs, rk, qidx, inv, items, counters, part_diag, lse_diag, part_off, lse_off,
-      sel;
+      sel, delta, part_dq;
   size_t total;
 };
 
-WsPlan plan(const moba::Problem& p, bool full) {
+// `full`: the query lists and the forward partials; `backward`: the query
+// lists and the backward's Δ and dQ partials instead of the forward partials.
+WsPlan plan(const moba::Problem& p, bool full, bool backward = false) {
   Layout L;
   WsPlan w;
   std::memset(&w, 0, sizeof(w));
@@ -145,10 +147,15 @@ WsPlan plan(const moba::Problem& p, bool full) {
     w.inv = L.add(hN * p.lmax * 4);
     w.items = L.add(p.max_items * sizeof(moba::WorkItem));
     w.counters = L.add(moba::kCounterInts * 4);
-    w.part_diag = L.add((hN + moba::kDumpRows) * p.D * es);
-    w.lse_diag = L.add((hN + moba::kDumpRows) * 4);
-    w.part_off = L.add((p.p_off + moba::kDumpRows) * p.D * es);
-    w.lse_off = L.add((p.p_off + moba::kDumpRows) * 4);
+    if (!backward) {
+      w.part_diag = L.add((hN + moba::kDumpRows) * p.D * es);
+      w.lse_diag = L.add((hN + moba::kDumpRows) * 4);
+      w.part_off = L.add((p.p_off + moba::kDumpRows) * p.D * es);
+      w.lse_off = L.add((p.p_off + moba::kDumpRows) * 4);
+    } else {
+      w.delta = L.add(hN * 4);
+      w.part_dq = L.add(p.p_off * p.D * 4);
+    }
     w.sel = L.add(hN * p.topk * 4);
   }
   w.total = L.total;
@@ -259,6 +266,62 @@ int prefill_impl(const void* q, const void* k, const void* v, void* out, float* 
   return finish(e, base, stream);
 }
 
+int backward_impl(const void* q, const void* k, const void* v, const void* out, const float* lse, const void* dout,
+                  void* dq, void* dk, void* dv, int64_t N, int32_t H, int32_t D, int32_t B, int32_t topk,
+                  hipStream_t stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || lse == nullptr || dout == nullptr ||
+      dq == nullptr || dk == nullptr || dv == nullptr)
+    return MOBA_ERR_INVALID_ARG;
+  int s = check_shape(N, H, D, B);
+  if (s != MOBA_OK) return s;
+  if ((s = check_topk(N, B, topk)) != MOBA_OK) return s;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return MOBA_ERR_UNSUPPORTED;
+  const moba::Problem p = make_problem(N, H, D, B, topk, false);
+  if (p.p_off >= (int64_t{1} << 31)) return MOBA_ERR_UNSUPPORTED;
+  DeviceState* st = nullptr;
+  if ((s = current_device(&st)) != MOBA_OK) return s;
+  const WsPlan w = plan(p, true, true);
+  char* base = nullptr;
+  if ((s = alloc_ws(st, w.total, stream, &base)) != MOBA_OK) return s;
+  moba::Workspace ws = bind(w, base, true);
+  moba::BwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = static_cast<const moba::bf16*>(q);
+  a.k = static_cast<const moba::bf16*>(k);
+  a.v = static_cast<const moba::bf16*>(v);
+  a.out = static_cast<const moba::bf16*>(out);
+  a.dout = static_cast<const moba::bf16*>(dout);
+  a.lse = lse;
+  a.dq = static_cast<moba::bf16*>(dq);
+  a.dk = static_cast<moba::bf16*>(dk);
+  a.dv = static_cast<moba::bf16*>(dv);
+  a.delta = reinterpret_cast<float*>(base + w.delta);
+  a.part_dq = reinterpret_cast<float*>(base + w.part_dq);
+  a.qidx = ws.qidx;
+  a.offs = ws.offs;
+  a.totals = ws.totals;
+  a.inv = ws.inv;
+  a.items = ws.items;
+  a.counters = ws.counters;
+  a.N = N;
+  a.H = H;
+  a.D = D;
+  a.B = B;
+  a.n = p.n;
+  a.topk = topk;
+  a.lmax = p.lmax;
+  a.max_items = p.lmax > 0 ? p.max_items : 0;
+  a.scale = 1.0f / std::sqrt(static_cast<float>(D));
+  a.scale_log2 = 1.4426950408889634f / std::sqrt(static_cast<float>(D));
+  hipError_t e = moba::launch_pool(k, false, ws.kbar, ws.kpieces, N, H, D, B, stream);
+  if (e == hipSuccess) e = moba::launch_gate(p, q, ws, ws.sel, true, st->num_cus, stream);
+  if (e == hipSuccess) e = moba::launch_csr(p, ws, ws.sel, stream);
+  if (e == hipSuccess) e = moba::launch_backward(a, stream);
+  return finish(e, base, stream);
+}
+
 int decode_impl(const void* q, const void* k, const void* v, const float* kbar, int32_t kbar_blocks, void* out,
                 float* lse, int32_t* sel, int64_t N, int32_t H, int32_t D, int32_t B, int32_t topk,
                 hipStream_t stream) {
@@ -365,6 +428,12 @@ int moba_decode_fwd(const void* q, const void* k, const void* v, const float* kb
                     float* lse, int32_t* sel, int64_t N, int32_t H, int32_t D, int32_t block_size, int32_t topk,
                     hipStream_t stream) {
   return decode_impl(q, k, v, kbar, kbar_blocks, out, lse, sel, N, H, D, block_size, topk, stream);
+}
+
+int moba_prefill_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, int64_t N, int32_t H, int32_t D,
+                     int32_t block_size, int32_t topk, hipStream_t stream) {
+  return backward_impl(q, k, v, out, lse, dout, dq, dk, dv, N, H, D, block_size, topk, stream);
 }
 
 const char* moba_status_string(int status) {

@@ -102,6 +102,15 @@ def make_qkv(N: int, H: int, D: int, seed, dtype: str = "bf16", scale: float = 1
     return q, k, v
 
 
+def make_grad(N: int, H: int, D: int, seed, dtype: str = "bf16", scale: float = 1.0):
+    """An upstream gradient dO for the backward pass: i.i.d. N(0, scale^2), [N, H, D]."""
+    rng = np.random.default_rng(seed)
+    g = _normal(rng, (N, H, D))
+    if scale != 1.0:
+        g *= np.float32(scale)
+    return round_to_bf16(g) if dtype == "bf16" else g
+
+
 def _per_head(N, H, D, seed_of_head, fill):
     q = np.empty((N, H, D), np.float32)
     k = np.empty((N, H, D), np.float32)

@@ -119,6 +119,23 @@ int moba_prefill_fwd_f32(const float* q, const float* k, const float* v, float* 
                          hipStream_t stream);
 
 /*
+ * Backward of the bf16 prefill: dq, dk, dv = the gradients of out (for the
+ * upstream gradient dout) with respect to q, k and v. The pages train and
+ * continually pretrain with MoBA (智东西 report, section 三); the top-k gate is
+ * piecewise constant and carries no gradient, so the same selection as the
+ * forward call (recomputed here from q and k) is held fixed and the gradients
+ * are those of the masked softmax attention over the attended keys. lse carries
+ * no upstream gradient. out and lse are those moba_prefill_fwd returned for the
+ * same q, k, v, block_size and topk.
+ * q, k, v, out, dout, dq, dk, dv: bf16 [N][H][D]; lse: fp32 [H][N] (natural
+ * log). Same shape limits and error behaviour as moba_prefill_fwd; dq, dk, dv
+ * are written in full (keys no query attends get zero gradients).
+ */
+int moba_prefill_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, int64_t N, int32_t H, int32_t D,
+                     int32_t block_size, int32_t topk, hipStream_t stream);
+
+/*
  * moba_prefill_fwd with stage timing: identical work and results, and, when
  * `events` is not NULL, events[0..MOBA_STAGE_EVENTS-1] (created by the caller
  * with hipEventCreate) are recorded on `stream` at the stage boundaries:
