@@ -158,3 +158,23 @@ def test_decode_argument_checks(lib):
         assert decode(lib, ptrs=tuple(ptrs)) == UNSUPPORTED
     assert decode(lib, kbar=A + 4, nb=7) == UNSUPPORTED
     assert decode(lib, sel=A + 8) == UNSUPPORTED
+
+
+def backward(lib, N=1024, H=2, D=128, B=128, topk=3, ptrs=(A,) * 9):
+    q, k, v, out, lse, dout, dq, dk, dv = ptrs
+    return lib.moba_prefill_bwd(q, k, v, out, lse, dout, dq, dk, dv, N, H, D, B, topk, None)
+
+
+def test_backward_argument_checks(lib):
+    for i in range(9):
+        ptrs = [A] * 9
+        ptrs[i] = None
+        assert backward(lib, ptrs=tuple(ptrs)) == INVALID, i
+    for kw in (dict(N=0), dict(H=0), dict(B=0), dict(topk=0), dict(N=1000)):
+        assert backward(lib, **kw) == INVALID, kw
+    for kw in (dict(D=96), dict(B=96, N=960), dict(H=70000), dict(N=128 * 100, topk=40)):
+        assert backward(lib, **kw) == UNSUPPORTED, kw
+    for i in range(9):
+        ptrs = [A] * 9
+        ptrs[i] = A + 4
+        assert backward(lib, ptrs=tuple(ptrs)) == UNSUPPORTED, i
