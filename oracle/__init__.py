@@ -17,4 +17,6 @@ from .moba_oracle import (  # noqa: F401
     select_blocks,
     select_row,
     sparsity,
+    topk_for_sparsity,
+    POOLINGS,
 )

@@ -71,23 +71,61 @@ def n_blocks(N: int, block_size: int) -> int:
     return N // block_size
 
 
-def pooled_keys(k: np.ndarray, block_size: int) -> np.ndarray:
-    """Exact (fp64) mean of the keys of every block: [H, n, D].
+POOLINGS = ("mean", "max", "weighted")
 
-    ``k`` is [N, H, D]; its values are widened exactly to fp64.
+
+def pooled_keys(k: np.ndarray, block_size: int, pooling: str = "mean", weights=None) -> np.ndarray:
+    """Representative key of every block (fp64): [H, n, D].
+
+    ``k`` is [N, H, D]; its values are widened exactly to fp64. ``pooling``:
+    "mean" (the pages' score_pooling), "max" (per-dimension maximum over the
+    block's keys) or "weighted" (sum of w_t k_t over the block divided by the
+    sum of w_t, with ``weights`` [H, N] non-negative per (head, token); a block
+    whose weights are all zero pools to the zero vector). The last two are the
+    variants the wzjinhao.cn MoBA article suggests trying in its closing
+    section.
     """
     N, H, D = k.shape
     n = n_blocks(N, block_size)
     k64 = np.asarray(k, dtype=np.float64).reshape(n, block_size, H, D)
-    total = np.zeros((n, H, D), dtype=np.float64)
-    for r in range(block_size):          # fixed order, one key of every block at a time
-        total += k64[:, r]
-    return np.ascontiguousarray((total / block_size).transpose(1, 0, 2))
+    if pooling == "mean":
+        total = np.zeros((n, H, D), dtype=np.float64)
+        for r in range(block_size):          # fixed order, one key of every block at a time
+            total += k64[:, r]
+        return np.ascontiguousarray((total / block_size).transpose(1, 0, 2))
+    if pooling == "max":
+        return np.ascontiguousarray(k64.max(axis=1).transpose(1, 0, 2))
+    if pooling == "weighted":
+        w64 = np.asarray(weights, dtype=np.float64)
+        if w64.shape != (H, N) or np.any(w64 < 0):
+            raise ValueError("weights must be a non-negative [H, N] array")
+        wb = w64.reshape(H, n, block_size).transpose(1, 2, 0)     # [n, B, H]
+        total = np.zeros((n, H, D), dtype=np.float64)
+        wsum = np.zeros((n, H), dtype=np.float64)
+        for r in range(block_size):
+            total += wb[:, r, :, None] * k64[:, r]
+            wsum += wb[:, r, :]
+        safe = np.where(wsum > 0, wsum, 1.0)
+        pooled = np.where((wsum > 0)[:, :, None], total / safe[:, :, None], 0.0)
+        return np.ascontiguousarray(pooled.transpose(1, 0, 2))
+    raise ValueError(f"unknown pooling {pooling!r}")
 
 
-def pooled_keys_fp32(k: np.ndarray, block_size: int) -> np.ndarray:
-    """The block mean keys rounded once to fp32 (the gate's precision): [H, n, D]."""
-    return pooled_keys(k, block_size).astype(np.float32)
+def pooled_keys_fp32(k: np.ndarray, block_size: int, pooling: str = "mean", weights=None) -> np.ndarray:
+    """The block representative keys rounded once to fp32 (the gate's precision): [H, n, D]."""
+    return pooled_keys(k, block_size, pooling, weights).astype(np.float32)
+
+
+def topk_for_sparsity(N: int, block_size: int, sparsity: float) -> int:
+    """Dynamic k: the top_k that keeps a late query's sparsity 1 - B k / N at
+    ``sparsity`` for this context length, k = round((1 - sparsity) N / B),
+    clamped to 1 .. n. The wzjinhao.cn MoBA article lets k grow with the
+    context (closing section) and pairs lengths with (block_size, top_k) at
+    about constant sparsity in its section 3 table."""
+    n = n_blocks(N, block_size)
+    if not 0.0 <= sparsity < 1.0:
+        raise ValueError("sparsity must be in [0, 1)")
+    return int(min(n, max(1, round((1.0 - sparsity) * N / block_size))))
 
 
 def gate_scores(q_rows: np.ndarray, kbar32_h: np.ndarray) -> np.ndarray:
@@ -118,16 +156,18 @@ def select_row(scores_row: np.ndarray, j: int, topk: int) -> list[int]:
 
 
 def select_blocks(q: np.ndarray, k: np.ndarray, block_size: int, topk: int,
-                  rows: np.ndarray | None = None, chunk: int = 65536):
+                  rows: np.ndarray | None = None, chunk: int = 65536, pooling: str = "mean", weights=None):
     """Selection of every (head, row): int32 [H, R, topk], ascending, -1 padded.
 
-    ``rows`` defaults to all N query rows. Also returns the fp32 mean keys.
+    ``rows`` defaults to all N query rows; ``pooling``/``weights`` pick the
+    block representative key (see ``pooled_keys``). Also returns the fp32
+    pooled keys.
     """
     N, H, D = q.shape
     n = n_blocks(N, block_size)
     if topk < 1:
         raise ValueError("topk must be >= 1")
-    kbar32 = pooled_keys_fp32(k, block_size)
+    kbar32 = pooled_keys_fp32(k, block_size, pooling, weights)
     rows = np.arange(N, dtype=np.int64) if rows is None else np.asarray(rows, np.int64)
     R = rows.shape[0]
     sel = np.full((H, R, topk), -1, dtype=np.int32)
@@ -260,12 +300,13 @@ def _attend_rowwise(q, k, v, block_size, sel, rows, out, lse, scale):
 
 
 def moba_ref(q, k, v, block_size: int, topk: int, sel=None, rows=None, method: str | None = None,
-             max_rows_chunk: int = 512):
+             max_rows_chunk: int = 512, pooling: str = "mean", weights=None):
     """fp64 MoBA causal prefill.
 
     Arguments are [N, H, D] arrays (float32 holding exact bf16 or fp32 values).
     ``sel`` optionally overrides the gate ([H, R, topk] int32 for the same rows).
     ``rows`` selects the query rows to evaluate (default: all).
+    ``pooling``/``weights`` pick the gate's block key (see ``pooled_keys``).
     ``method`` picks one of three evaluations of the same softmax over A(t):
     "dense" (masked logits against all keys up to the row's block; the default
     for all rows), "blocks" (logits of each chosen block for the rows that
@@ -281,7 +322,8 @@ def moba_ref(q, k, v, block_size: int, topk: int, sel=None, rows=None, method: s
     all_rows = rows is None
     rows = np.arange(N, dtype=np.int64) if all_rows else np.asarray(rows, np.int64)
     if sel is None:
-        sel, _ = select_blocks(q, k, block_size, topk, rows=None if all_rows else rows)
+        sel, _ = select_blocks(q, k, block_size, topk, rows=None if all_rows else rows, pooling=pooling,
+                               weights=weights)
     if method is None:
         method = "dense" if all_rows else "blocks"
     scale = 1.0 / math.sqrt(D)
@@ -449,7 +491,8 @@ def _backward_by_block(q, k, v, dout, block_size, sel, heads, dq, dk, dv, scale)
             dv[b * B:(b + 1) * B, oh] += p.T @ doh[ridx]
 
 
-def moba_backward_ref(q, k, v, dout, block_size: int, topk: int, sel=None, heads=None, method: str = "dense"):
+def moba_backward_ref(q, k, v, dout, block_size: int, topk: int, sel=None, heads=None, method: str = "dense",
+                      pooling: str = "mean", weights=None):
     """fp64 gradients of the MoBA causal prefill output.
 
     ``dout`` [N, H, D] is the upstream gradient of ``out``; the lse output
@@ -465,7 +508,7 @@ def moba_backward_ref(q, k, v, dout, block_size: int, topk: int, sel=None, heads
     N, H, D = q.shape
     n_blocks(N, block_size)
     if sel is None:
-        sel, _ = select_blocks(q, k, block_size, topk)
+        sel, _ = select_blocks(q, k, block_size, topk, pooling=pooling, weights=weights)
     heads = list(range(H)) if heads is None else [int(h) for h in heads]
     softmax_scale = 1.0 / math.sqrt(D)
     dq = np.zeros((N, len(heads), D), np.float64)

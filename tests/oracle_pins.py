@@ -46,7 +46,7 @@ def _t64(x):
 # independent brute force
 # ---------------------------------------------------------------------------
 
-def brute_selection(q, k, B, topk):
+def brute_selection(q, k, B, topk, kbar=None):
     """Top-k by exhaustive subset search, computed with torch (not numpy).
 
     For each query the chosen past blocks are the (k-1)-subset of eligible
@@ -57,8 +57,9 @@ def brute_selection(q, k, B, topk):
     """
     N, H, D = q.shape
     n = N // B
-    kt = _t64(k).reshape(n, B, H, D)
-    kbar = kt.mean(dim=1).to(torch.float32).to(torch.float64)     # [n, H, D]
+    if kbar is None:
+        kt = _t64(k).reshape(n, B, H, D)
+        kbar = kt.mean(dim=1).to(torch.float32).to(torch.float64)     # [n, H, D]
     sel = np.full((H, N, topk), -1, np.int64)
     for h in range(H):
         sc = (_t64(q[:, h, :]) @ kbar[:, h, :].T).to(torch.float32).to(torch.float64).numpy()
@@ -540,6 +541,67 @@ def pin_backward_methods_agree(m):
         assert np.allclose(x, z[:, [2, 0]], atol=1e-12, rtol=0)
 
 
+# ---------------------------------------------------------------------------
+# pooling variants and dynamic k
+# ---------------------------------------------------------------------------
+
+def _torch_pool(k, B, pooling, weights=None):
+    """Block keys through torch (fp64), [n, H, D]: amax, or the weighted average."""
+    N, H, D = k.shape
+    kt = _t64(k).reshape(N // B, B, H, D)
+    if pooling == "max":
+        return kt.amax(dim=1)
+    wt = _t64(weights).T.reshape(N // B, B, H)                       # [n, B, H]
+    return torch.einsum("nbh,nbhd->nhd", wt, kt) / wt.sum(dim=1)[:, :, None]
+
+
+def pin_pooling_max(m):
+    """Max pooling: torch amax per block, and the selection it leads to by exhaustive search."""
+    for N, H, D, B, topk, seed in [(32, 2, 4, 4, 3, 71), (48, 1, 4, 8, 2, 72)]:
+        q, k, v = _rand(N, H, D, seed)
+        ref = _torch_pool(k, B, "max").permute(1, 0, 2).numpy()
+        assert np.array_equal(m.pooled_keys(k, B, "max"), ref)
+        sel, _ = m.select_blocks(q, k, B, topk, pooling="max")
+        kb = _torch_pool(k, B, "max").to(torch.float32).to(torch.float64)
+        assert np.array_equal(sel, brute_selection(q, k, B, topk, kbar=kb))
+        out, _, _ = m.moba_ref(q, k, v, B, topk, pooling="max")
+        bout, _ = brute_attention(q, k, v, B, brute_selection(q, k, B, topk, kbar=kb))
+        assert np.allclose(out, bout, atol=1e-12, rtol=0)
+
+
+def pin_pooling_weighted(m):
+    """Weighted pooling: the weighted average through torch; equal weights give the mean,
+    one-hot weights pick a key, all-zero weights give zero; the selection by exhaustive search."""
+    N, H, D, B, topk = 48, 2, 4, 8, 3
+    q, k, v = _rand(N, H, D, 73)
+    rng = np.random.default_rng(74)
+    w = rng.uniform(0.0, 2.0, (H, N))
+    ref = _torch_pool(k, B, "weighted", w).permute(1, 0, 2).numpy()
+    assert np.allclose(m.pooled_keys(k, B, "weighted", w), ref, atol=1e-14, rtol=0)
+    assert np.array_equal(m.pooled_keys(k, B, "weighted", np.full((H, N), 0.5)), m.pooled_keys(k, B))
+    onehot = np.zeros((H, N))
+    onehot[:, 3::B] = 1.0
+    assert np.array_equal(m.pooled_keys(k, B, "weighted", onehot), np.asarray(k[3::B], np.float64).transpose(1, 0, 2))
+    zero = w.copy()
+    zero[:, :B] = 0.0
+    assert np.all(m.pooled_keys(k, B, "weighted", zero)[:, 0] == 0.0)
+    sel, _ = m.select_blocks(q, k, B, topk, pooling="weighted", weights=w)
+    kb = _torch_pool(k, B, "weighted", w).to(torch.float32).to(torch.float64)
+    assert np.array_equal(sel, brute_selection(q, k, B, topk, kbar=kb))
+
+
+def pin_topk_for_sparsity(m):
+    """Dynamic k reproduces the pages' (context, block_size, top_k) table from its sparsity
+    column, and k does not shrink as the context grows."""
+    for r in golden()["sparsity_table"]["rows"]:
+        assert m.topk_for_sparsity(r["N"], r["block_size"], r["sparsity_percent_1dp"] / 100) == r["top_k"]
+    snip = golden()["config_snippet"]
+    assert m.topk_for_sparsity(snip["context_length"], snip["block_size"], snip["sparsity_percent_1dp"] / 100) \
+        == snip["top_k"]
+    ks = [m.topk_for_sparsity(N, 512, 0.953) for N in (512, 4096, 32768, 262144, 1048576)]
+    assert ks == sorted(ks) and ks[0] == 1 and ks[-1] == round(0.047 * 2048)
+
+
 ALL_PINS = [
     pin_bruteforce_tiny, pin_full_causal, pin_block_diagonal, pin_first_token, pin_constant_v,
     pin_zero_query, pin_invariants, pin_pages_worked_example, pin_pages_sparsity_table,
@@ -547,5 +609,6 @@ ALL_PINS = [
     pin_gate_rounding, pin_row_mode_matches, pin_decode_full_attention, pin_decode_own_block,
     pin_decode_first_token, pin_decode_brute_selection, pin_decode_matches_prefill_row,
     pin_backward_full_causal, pin_backward_block_diagonal, pin_backward_brute, pin_backward_finite_difference,
-    pin_backward_invariants, pin_backward_methods_agree,
+    pin_backward_invariants, pin_backward_methods_agree, pin_pooling_max, pin_pooling_weighted,
+    pin_topk_for_sparsity,
 ]

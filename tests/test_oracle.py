@@ -43,8 +43,8 @@ MUTATIONS = {
     "own_block_full": ("parts.append(np.arange(j * block_size, t + 1))",
                        "parts.append(np.arange(j * block_size, (j + 1) * block_size))"),
     "no_fp32_gate_rounding": ("return s.astype(np.float32)", "return s"),
-    "pool_fp32_not_rounded": ("return pooled_keys(k, block_size).astype(np.float32)",
-                              "return pooled_keys(k, block_size).astype(np.float16).astype(np.float32)"),
+    "pool_fp32_not_rounded": ("return pooled_keys(k, block_size, pooling, weights).astype(np.float32)",
+                              "return pooled_keys(k, block_size, pooling, weights).astype(np.float16).astype(np.float32)"),
     "pad_with_zero": ("sel = np.full((H, R, topk), -1, dtype=np.int32)",
                       "sel = np.full((H, R, topk), 0, dtype=np.int32)"),
     "transposed_scores": ("s = np.asarray(q_rows, np.float64) @ np.asarray(kbar32_h, np.float64).T",
@@ -62,6 +62,12 @@ MUTATIONS = {
     "decode_wrong_query_head": ("logits = (k_att @ np.asarray(q_new[h], np.float64)) * inv_sqrt_d",
                                 "logits = (k_att @ np.asarray(q_new[(h + 1) % H], np.float64)) * inv_sqrt_d"),
     "decode_scale_1_over_d": ("inv_sqrt_d = 1.0 / math.sqrt(D)", "inv_sqrt_d = 1.0 / D"),
+    "pool_max_is_min": ("return np.ascontiguousarray(k64.max(axis=1).transpose(1, 0, 2))",
+                        "return np.ascontiguousarray(k64.min(axis=1).transpose(1, 0, 2))"),
+    "weighted_not_normalised": ("total / safe[:, :, None], 0.0)", "total, 0.0)"),
+    "weighted_weights_of_wrong_head": ("wb = w64.reshape(H, n, block_size).transpose(1, 2, 0)",
+                                       "wb = w64[::-1].reshape(H, n, block_size).transpose(1, 2, 0)"),
+    "dynamic_k_rounds_up": ("round((1.0 - sparsity) * N / block_size)", "math.ceil((1.0 - sparsity) * N / block_size)"),
     "backward_scale_1_over_d": ("softmax_scale = 1.0 / math.sqrt(D)", "softmax_scale = 1.0 / D"),
     "backward_drops_row_sum": ("dl = p * (dp - np.sum(p * dp, axis=1, keepdims=True))", "dl = p * dp"),
     "backward_dk_unscaled": ("dk[:nk, oh] += scale * (dl.T @ qh)", "dk[:nk, oh] += dl.T @ qh"),
