@@ -12,6 +12,7 @@ library records on its stream, the roofline of the dominant kernel (the
 past-block attention launch), and the fp64 oracle timed on the host on a
 sample of query rows.
 
+A ``pooling`` object times the prefill with max and weighted block pooling.
 A ``backward`` object times ``moba_prefill_bwd`` (dQ, dK, dV for a seeded
 upstream gradient) on the same inputs, effective TFLOP/s counted as 2.5x the
 forward's attended-pair work. A ``decode`` object beside it times ``moba_decode_fwd`` for the newest token of
@@ -153,6 +154,31 @@ def backward_bench(moba, w, qd, kd, vd, out, lse, steps: int, warmup: int):
             "includes": "block mean-pool, gate, query lists (recomputed), delta, dK/dV, dQ"}
 
 
+def pooling_bench(moba, w, qd, kd, vd, steps: int):
+    """The prefill with max and with weighted block pooling (weights: seeded
+    uniform [0, 1) per head and token); only the pool stage differs."""
+    import torch
+    wts = torch.from_numpy(np.random.default_rng([403, 0]).uniform(0.0, 1.0, (w.H, w.N)).astype(np.float32))
+    wts = wts.to(qd.device)
+    flops = 4.0 * w.D * effective_pairs(w.N, w.block_size, w.topk) * w.H
+    res = {}
+    for pooling in ("max", "weighted"):
+        args = (qd, kd, vd, w.block_size, w.topk, pooling, wts if pooling == "weighted" else None)
+        for _ in range(3):
+            moba.prefill_pooled(*args)
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(steps):
+            moba.prefill_pooled(*args)
+        stop.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(stop) / steps
+        res[pooling] = {"ms_per_step": ms, "effective_tflops": flops / (ms * 1e-3) / 1e12}
+    return res
+
+
 def cpu_baseline(w, q, k, v, gpu_out, gpu_lse, target_s: float):
     """The fp64 oracle as it stands, on a seeded sample of query rows."""
     import threadpoolctl
@@ -201,6 +227,8 @@ def main():
     ap.add_argument("--workload", default="h32")
     ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--pooling", choices=("on", "off"), default="on",
+                    help="also time the prefill with max and weighted block pooling")
     ap.add_argument("--backward", choices=("on", "off"), default="on",
                     help="also time the backward pass on the same workload")
     ap.add_argument("--decode", choices=("on", "off"), default="on",
@@ -323,6 +351,12 @@ def main():
         },
         "device": info,
     }
+
+    if args.pooling == "on":
+        result["pooling"] = pooling_bench(moba, w, qd, kd, vd, max(5, args.steps // 2))
+        pl = result["pooling"]
+        print(f"[bench] pooled prefill: max {pl['max']['ms_per_step']:.3f} ms, "
+              f"weighted {pl['weighted']['ms_per_step']:.3f} ms", file=sys.stderr, flush=True)
 
     if args.backward == "on":
         result["backward"] = backward_bench(moba, w, qd, kd, vd, out, lse, args.steps, args.warmup)

@@ -40,6 +40,11 @@ _SIGNATURES = {
     "moba_prefill_fwd_timed": [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P],
     "moba_decode_fwd": [_P, _P, _P, _P, _I32, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P],
     "moba_prefill_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P],
+    "moba_block_pool_keys": [_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P],
+    "moba_gate_topk_pooled": [_P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _P],
+    "moba_prefill_fwd_pooled": [_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _P],
+    "moba_prefill_bwd_pooled": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _P],
+    "moba_topk_for_sparsity": [_I64, _I32, ctypes.c_double],
     "moba_status_string": [ctypes.c_int],
     "moba_last_hip_error": [],
 }
@@ -69,6 +74,7 @@ def load_library():
             fn = getattr(lib, name)
             fn.argtypes = args
             fn.restype = ctypes.c_char_p if name == "moba_status_string" else ctypes.c_int
+        lib.moba_topk_for_sparsity.restype = ctypes.c_int32
         _lib = lib
     return _lib
 
@@ -208,7 +214,79 @@ def prefill(q, k, v, block_size: int, topk: int, out=None, lse=None, events: "St
     return out, lse
 
 
-def prefill_backward(q, k, v, out, lse, dout, block_size: int, topk: int, dq=None, dk=None, dv=None):
+POOLING = {"mean": 0, "max": 1, "weighted": 2}
+
+
+def _pool_args(pooling, weights, H, N, device):
+    import torch
+    if pooling not in POOLING:
+        raise ValueError(f"pooling must be one of {sorted(POOLING)}")
+    if pooling == "weighted":
+        if weights is None or weights.shape != (H, N) or weights.dtype != torch.float32 \
+                or not weights.is_contiguous() or weights.device != device:
+            raise ValueError("weighted pooling needs contiguous fp32 [H, N] weights on the inputs' device")
+        return POOLING[pooling], weights.data_ptr()
+    return POOLING[pooling], None
+
+
+def block_pool_keys(k, block_size: int, pooling: str = "mean", weights=None):
+    """Pooled block keys (bf16 k), fp32 ``[H, N // block_size, D]``; ``pooling`` is
+    "mean", "max" or "weighted" (``weights`` fp32 [H, N], non-negative)."""
+    import torch
+    N, H, D, f32 = _check_qkv(k)
+    if f32:
+        raise TypeError("block_pool_keys takes bf16 keys")
+    mode, wp = _pool_args(pooling, weights, H, N, k.device)
+    lib = load_library()
+    kbar = torch.empty((H, max(N // block_size, 1), D), dtype=torch.float32, device=k.device)
+    _check(lib.moba_block_pool_keys(k.data_ptr(), wp, kbar.data_ptr(), N, H, D, block_size, mode, _stream(k.device)),
+           "moba_block_pool_keys")
+    return kbar
+
+
+def gate_topk_pooled(q, k, block_size: int, topk: int, pooling: str = "mean", weights=None):
+    """:func:`gate_topk` (bf16) with the block keys pooled by ``pooling``."""
+    import torch
+    N, H, D, f32 = _check_qkv(q, k)
+    if f32:
+        raise TypeError("the pooled gate takes bf16 tensors")
+    mode, wp = _pool_args(pooling, weights, H, N, q.device)
+    lib = load_library()
+    sel = torch.empty((H, N, max(topk, 1)), dtype=torch.int32, device=q.device)
+    _check(lib.moba_gate_topk_pooled(q.data_ptr(), k.data_ptr(), wp, sel.data_ptr(), N, H, D, block_size, topk, mode,
+                                     _stream(q.device)), "moba_gate_topk_pooled")
+    return sel
+
+
+def prefill_pooled(q, k, v, block_size: int, topk: int, pooling: str = "mean", weights=None, out=None, lse=None):
+    """:func:`prefill` (bf16) with the gate's block keys pooled by ``pooling``."""
+    import torch
+    N, H, D, f32 = _check_qkv(q, k, v)
+    if f32:
+        raise TypeError("the pooled prefill takes bf16 tensors")
+    mode, wp = _pool_args(pooling, weights, H, N, q.device)
+    lib = load_library()
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [H, N] tensor")
+    _check(lib.moba_prefill_fwd_pooled(q.data_ptr(), k.data_ptr(), v.data_ptr(), wp, out.data_ptr(), lse.data_ptr(),
+                                       N, H, D, block_size, topk, mode, _stream(q.device)), "moba_prefill_fwd_pooled")
+    return out, lse
+
+
+def topk_for_sparsity(N: int, block_size: int, sparsity: float) -> int:
+    """Dynamic k: the top_k keeping a late query's sparsity at ``sparsity`` (host only)."""
+    k = load_library().moba_topk_for_sparsity(N, block_size, sparsity)
+    if k < 1:
+        raise MobaError(-k, "moba_topk_for_sparsity")
+    return k
+
+
+def prefill_backward(q, k, v, out, lse, dout, block_size: int, topk: int, dq=None, dk=None, dv=None,
+                     pooling: str = "mean", weights=None):
     """Gradients of the bf16 MoBA prefill output: returns ``(dq, dk, dv)`` [N, H, D] bf16.
 
     ``out`` and ``lse`` are what :func:`prefill` returned for the same inputs;
@@ -228,9 +306,16 @@ def prefill_backward(q, k, v, out, lse, dout, block_size: int, topk: int, dq=Non
             raise ValueError("dq, dk, dv must be contiguous tensors like q")
         grads.append(g)
     lib = load_library()
-    _check(lib.moba_prefill_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                                dout.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(),
-                                N, H, D, block_size, topk, _stream(q.device)), "moba_prefill_bwd")
+    if pooling == "mean":
+        _check(lib.moba_prefill_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                    dout.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(),
+                                    N, H, D, block_size, topk, _stream(q.device)), "moba_prefill_bwd")
+    else:
+        mode, wp = _pool_args(pooling, weights, H, N, q.device)
+        _check(lib.moba_prefill_bwd_pooled(q.data_ptr(), k.data_ptr(), v.data_ptr(), wp, out.data_ptr(),
+                                           lse.data_ptr(), dout.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(),
+                                           grads[2].data_ptr(), N, H, D, block_size, topk, mode, _stream(q.device)),
+               "moba_prefill_bwd_pooled")
     return tuple(grads)
 
 

@@ -23,8 +23,12 @@ struct Problem {
   bool is_f32;
 };
 
+// Block pooling modes (MOBA_POOL_* in moba.h).
+constexpr int kPoolMean = 0, kPoolMax = 1, kPoolWeighted = 2;
+// Block keys (and their 3-way bf16 split when `pieces` is not null). `weights`
+// [H][N] is read in the weighted mode only.
 hipError_t launch_pool(const void* k, bool is_f32, float* kbar, bf16* pieces, int64_t N, int H, int D, int B,
-                       hipStream_t stream);
+                       hipStream_t stream, int mode = kPoolMean, const float* weights = nullptr);
 
 // Gate + causal top-k; writes sel and, when `ws_csr` is true, the per-tile
 // counts and in-tile ranks of the off-diagonal selections.

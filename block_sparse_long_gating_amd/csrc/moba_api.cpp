@@ -204,24 +204,41 @@ int finish(hipError_t launch_error, char* ws, hipStream_t stream) {
   return MOBA_OK;
 }
 
+// Block pooling of the gate's keys: a MOBA_POOL_* mode and, for the weighted
+// mode, the caller's [H][N] fp32 weights.
+struct Pooling {
+  int mode = MOBA_POOL_MEAN;
+  const float* weights = nullptr;
+};
+
+int check_pooling(const Pooling& pl) {
+  if (pl.mode != MOBA_POOL_MEAN && pl.mode != MOBA_POOL_MAX && pl.mode != MOBA_POOL_WEIGHTED)
+    return MOBA_ERR_INVALID_ARG;
+  if (pl.mode == MOBA_POOL_WEIGHTED && pl.weights == nullptr) return MOBA_ERR_INVALID_ARG;
+  if (pl.mode == MOBA_POOL_WEIGHTED && reinterpret_cast<uintptr_t>(pl.weights) % 4 != 0) return MOBA_ERR_UNSUPPORTED;
+  return MOBA_OK;
+}
+
 int block_mean_keys_impl(const void* k, float* kbar, int64_t N, int32_t H, int32_t D, int32_t B, hipStream_t stream,
-                         bool is_f32) {
+                         bool is_f32, const Pooling& pl = Pooling()) {
   if (k == nullptr || kbar == nullptr) return MOBA_ERR_INVALID_ARG;
   int s = check_shape(N, H, D, B);
   if (s != MOBA_OK) return s;
+  if ((s = check_pooling(pl)) != MOBA_OK) return s;
   if (!aligned16(k) || !aligned16(kbar)) return MOBA_ERR_UNSUPPORTED;
   DeviceState* st = nullptr;
   if ((s = current_device(&st)) != MOBA_OK) return s;
-  hipError_t e = moba::launch_pool(k, is_f32, kbar, nullptr, N, H, D, B, stream);
+  hipError_t e = moba::launch_pool(k, is_f32, kbar, nullptr, N, H, D, B, stream, pl.mode, pl.weights);
   return e == hipSuccess ? MOBA_OK : hip_fail(e);
 }
 
 int gate_impl(const void* q, const void* k, int32_t* sel, int64_t N, int32_t H, int32_t D, int32_t B, int32_t topk,
-              hipStream_t stream, bool is_f32) {
+              hipStream_t stream, bool is_f32, const Pooling& pl = Pooling()) {
   if (q == nullptr || k == nullptr || sel == nullptr) return MOBA_ERR_INVALID_ARG;
   int s = check_shape(N, H, D, B);
   if (s != MOBA_OK) return s;
   if ((s = check_topk(N, B, topk)) != MOBA_OK) return s;
+  if ((s = check_pooling(pl)) != MOBA_OK) return s;
   if (!aligned16(q) || !aligned16(k) || !aligned16(sel)) return MOBA_ERR_UNSUPPORTED;
   DeviceState* st = nullptr;
   if ((s = current_device(&st)) != MOBA_OK) return s;
@@ -230,17 +247,20 @@ int gate_impl(const void* q, const void* k, int32_t* sel, int64_t N, int32_t H, 
   char* base = nullptr;
   if ((s = alloc_ws(st, w.total, stream, &base)) != MOBA_OK) return s;
   moba::Workspace ws = bind(w, base, false);
-  hipError_t e = moba::launch_pool(k, is_f32, ws.kbar, is_f32 ? nullptr : ws.kpieces, N, H, D, B, stream);
+  hipError_t e =
+      moba::launch_pool(k, is_f32, ws.kbar, is_f32 ? nullptr : ws.kpieces, N, H, D, B, stream, pl.mode, pl.weights);
   if (e == hipSuccess) e = moba::launch_gate(p, q, ws, sel, false, st->num_cus, stream);
   return finish(e, base, stream);
 }
 
 int prefill_impl(const void* q, const void* k, const void* v, void* out, float* lse, int64_t N, int32_t H, int32_t D,
-                 int32_t B, int32_t topk, hipStream_t stream, bool is_f32, hipEvent_t* events = nullptr) {
+                 int32_t B, int32_t topk, hipStream_t stream, bool is_f32, hipEvent_t* events = nullptr,
+                 const Pooling& pl = Pooling()) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || lse == nullptr) return MOBA_ERR_INVALID_ARG;
   int s = check_shape(N, H, D, B);
   if (s != MOBA_OK) return s;
   if ((s = check_topk(N, B, topk)) != MOBA_OK) return s;
+  if ((s = check_pooling(pl)) != MOBA_OK) return s;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
     return MOBA_ERR_UNSUPPORTED;
   const moba::Problem p = make_problem(N, H, D, B, topk, is_f32);
@@ -253,7 +273,8 @@ int prefill_impl(const void* q, const void* k, const void* v, void* out, float* 
   moba::Workspace ws = bind(w, base, true);
   auto mark = [&](int i) { return events && events[i] ? hipEventRecord(events[i], stream) : hipSuccess; };
   hipError_t e = mark(0);
-  if (e == hipSuccess) e = moba::launch_pool(k, is_f32, ws.kbar, is_f32 ? nullptr : ws.kpieces, N, H, D, B, stream);
+  if (e == hipSuccess)
+    e = moba::launch_pool(k, is_f32, ws.kbar, is_f32 ? nullptr : ws.kpieces, N, H, D, B, stream, pl.mode, pl.weights);
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) e = moba::launch_gate(p, q, ws, ws.sel, true, st->num_cus, stream);
   if (e == hipSuccess) e = mark(2);
@@ -268,13 +289,14 @@ int prefill_impl(const void* q, const void* k, const void* v, void* out, float* 
 
 int backward_impl(const void* q, const void* k, const void* v, const void* out, const float* lse, const void* dout,
                   void* dq, void* dk, void* dv, int64_t N, int32_t H, int32_t D, int32_t B, int32_t topk,
-                  hipStream_t stream) {
+                  hipStream_t stream, const Pooling& pl = Pooling()) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || lse == nullptr || dout == nullptr ||
       dq == nullptr || dk == nullptr || dv == nullptr)
     return MOBA_ERR_INVALID_ARG;
   int s = check_shape(N, H, D, B);
   if (s != MOBA_OK) return s;
   if ((s = check_topk(N, B, topk)) != MOBA_OK) return s;
+  if ((s = check_pooling(pl)) != MOBA_OK) return s;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse) || !aligned16(dout) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return MOBA_ERR_UNSUPPORTED;
@@ -315,7 +337,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* out, 
   a.max_items = p.lmax > 0 ? p.max_items : 0;
   a.scale = 1.0f / std::sqrt(static_cast<float>(D));
   a.scale_log2 = 1.4426950408889634f / std::sqrt(static_cast<float>(D));
-  hipError_t e = moba::launch_pool(k, false, ws.kbar, ws.kpieces, N, H, D, B, stream);
+  hipError_t e = moba::launch_pool(k, false, ws.kbar, ws.kpieces, N, H, D, B, stream, pl.mode, pl.weights);
   if (e == hipSuccess) e = moba::launch_gate(p, q, ws, ws.sel, true, st->num_cus, stream);
   if (e == hipSuccess) e = moba::launch_csr(p, ws, ws.sel, stream);
   if (e == hipSuccess) e = moba::launch_backward(a, stream);
@@ -434,6 +456,48 @@ int moba_prefill_bwd(const void* q, const void* k, const void* v, const void* ou
                      const void* dout, void* dq, void* dk, void* dv, int64_t N, int32_t H, int32_t D,
                      int32_t block_size, int32_t topk, hipStream_t stream) {
   return backward_impl(q, k, v, out, lse, dout, dq, dk, dv, N, H, D, block_size, topk, stream);
+}
+
+int moba_block_pool_keys(const void* k, const float* weights, float* kbar, int64_t N, int32_t H, int32_t D,
+                         int32_t block_size, int32_t pooling, hipStream_t stream) {
+  Pooling pl;
+  pl.mode = pooling;
+  pl.weights = weights;
+  return block_mean_keys_impl(k, kbar, N, H, D, block_size, stream, false, pl);
+}
+
+int moba_gate_topk_pooled(const void* q, const void* k, const float* weights, int32_t* sel, int64_t N, int32_t H,
+                          int32_t D, int32_t block_size, int32_t topk, int32_t pooling, hipStream_t stream) {
+  Pooling pl;
+  pl.mode = pooling;
+  pl.weights = weights;
+  return gate_impl(q, k, sel, N, H, D, block_size, topk, stream, false, pl);
+}
+
+int moba_prefill_fwd_pooled(const void* q, const void* k, const void* v, const float* weights, void* out, float* lse,
+                            int64_t N, int32_t H, int32_t D, int32_t block_size, int32_t topk, int32_t pooling,
+                            hipStream_t stream) {
+  Pooling pl;
+  pl.mode = pooling;
+  pl.weights = weights;
+  return prefill_impl(q, k, v, out, lse, N, H, D, block_size, topk, stream, false, nullptr, pl);
+}
+
+int moba_prefill_bwd_pooled(const void* q, const void* k, const void* v, const float* weights, const void* out,
+                            const float* lse, const void* dout, void* dq, void* dk, void* dv, int64_t N, int32_t H,
+                            int32_t D, int32_t block_size, int32_t topk, int32_t pooling, hipStream_t stream) {
+  Pooling pl;
+  pl.mode = pooling;
+  pl.weights = weights;
+  return backward_impl(q, k, v, out, lse, dout, dq, dk, dv, N, H, D, block_size, topk, stream, pl);
+}
+
+int32_t moba_topk_for_sparsity(int64_t N, int32_t block_size, double sparsity) {
+  if (N < 1 || block_size < 1 || N % block_size != 0 || !(sparsity >= 0.0 && sparsity < 1.0))
+    return -MOBA_ERR_INVALID_ARG;
+  const int64_t n = N / block_size;
+  const double kk = std::nearbyint((1.0 - sparsity) * static_cast<double>(N) / static_cast<double>(block_size));
+  return static_cast<int32_t>(std::min<double>(static_cast<double>(n), std::max(1.0, kk)));
 }
 
 const char* moba_status_string(int status) {

@@ -1,8 +1,12 @@
-// Block mean-pool of the keys: kbar[h][i][:] = mean of the block_size keys of block i.
+// Block pooling of the keys: kbar[h][i][:] = the representative key of block i.
 //
 // Mean pooling gives each block the "representative" key the gate scores
 // against (wzjinhao.cn MoBA article, section 3, score_pooling = mean; pomoai MoBA
-// overview, "核心原理" step 2). HBM-bound: every key is read exactly once.
+// overview, "核心原理" step 2). The same article's closing section suggests
+// max or weighted pooling instead: the per-dimension maximum over the block's
+// keys, or the average of the block's keys under non-negative per-(head,
+// token) weights (all-zero weights pool to zero). HBM-bound: every key is read
+// exactly once.
 //
 // One workgroup per (block, group of up to 8 heads). Each thread owns 8
 // consecutive dims of one head on a strided subset of the block's rows
@@ -37,10 +41,12 @@ __device__ __forceinline__ void load8<float>(const float* p, float (&x)[8]) {
   x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void pool_keys_kernel(const T* __restrict__ k, float* __restrict__ kbar,
-                                                        bf16* __restrict__ pieces, int H, int B, int n, int hg) {
+template <typename T, int D, int kMode>
+__global__ __launch_bounds__(256) void pool_keys_kernel(const T* __restrict__ k, const float* __restrict__ weights,
+                                                        float* __restrict__ kbar, bf16* __restrict__ pieces, int H,
+                                                        int B, int n, int hg) {
   __shared__ double red[256][8];
+  __shared__ double redw[kMode == kPoolWeighted ? 256 : 1];
 
   const int i = blockIdx.x;
   const int h0 = blockIdx.y * hg;             // this workgroup's heads h0 .. h0 + hg - 1
@@ -52,9 +58,29 @@ __global__ __launch_bounds__(256) void pool_keys_kernel(const T* __restrict__ k,
   // The hg heads of one token are contiguous: each row pass reads hg * 2D bytes in one run.
   const T* base = k + (static_cast<int64_t>(i) * B * H + h0) * D + c * 8;
 
+  const int hc = h0 + c / (D / 8);            // this thread's head
+  // Weights of this thread's head for the block's tokens (weighted mode).
+  const float* wrow =
+      kMode == kPoolWeighted ? weights + static_cast<int64_t>(hc) * n * B + static_cast<int64_t>(i) * B : nullptr;
+
   double acc[8];
+  double wacc = 0.0;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+  for (int e = 0; e < 8; ++e) acc[e] = kMode == kPoolMax ? -INFINITY : 0.0;
+  auto add = [&](const float (&x)[8], int row) {
+    if (kMode == kPoolMax) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmax(acc[e], static_cast<double>(x[e]));
+    } else if (kMode == kPoolWeighted) {
+      const double wt = static_cast<double>(wrow[row]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += wt * static_cast<double>(x[e]);   // exact product
+      wacc += wt;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += static_cast<double>(x[e]);
+    }
+  };
 
   // Eight independent 16-byte loads in flight per thread, added in row order.
   int r = r0;
@@ -63,35 +89,39 @@ __global__ __launch_bounds__(256) void pool_keys_kernel(const T* __restrict__ k,
 #pragma unroll
     for (int u = 0; u < 8; ++u) load8<T>(base + static_cast<int64_t>(r + u * rows_per_pass) * row_stride, x[u]);
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += static_cast<double>(x[u][e]);
+    for (int u = 0; u < 8; ++u) add(x[u], r + u * rows_per_pass);
   }
   for (; r < B; r += rows_per_pass) {
     float x0[8];
     load8<T>(base + static_cast<int64_t>(r) * row_stride, x0);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += static_cast<double>(x0[e]);
+    add(x0, r);
   }
 
 #pragma unroll
   for (int e = 0; e < 8; ++e) red[threadIdx.x][e] = acc[e];
+  if (kMode == kPoolWeighted) redw[threadIdx.x] = wacc;
   __syncthreads();
 
   if (threadIdx.x < chunks) {
     double s[8];
+    double ws = 0.0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s[e] = 0.0;
+    for (int e = 0; e < 8; ++e) s[e] = kMode == kPoolMax ? -INFINITY : 0.0;
     for (int g = 0; g < rows_per_pass; ++g) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s[e] += red[g * chunks + c][e];
+      for (int e = 0; e < 8; ++e)
+        s[e] = kMode == kPoolMax ? fmax(s[e], red[g * chunks + c][e]) : s[e] + red[g * chunks + c][e];
+      if (kMode == kPoolWeighted) ws += redw[g * chunks + c];
     }
-    const int h = h0 + c / (D / 8);
+    const int h = hc;
     const int d0 = (c % (D / 8)) * 8;
     const int64_t o = (static_cast<int64_t>(h) * n + i) * D + d0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float m = static_cast<float>(s[e] / static_cast<double>(B));
+      float m;
+      if (kMode == kPoolMax) m = static_cast<float>(s[e]);
+      else if (kMode == kPoolWeighted) m = ws > 0.0 ? static_cast<float>(s[e] / ws) : 0.f;
+      else m = static_cast<float>(s[e] / static_cast<double>(B));
       kbar[o + e] = m;
       if (pieces != nullptr) {
         const bf16 hi = static_cast<bf16>(m);
@@ -108,10 +138,21 @@ __global__ __launch_bounds__(256) void pool_keys_kernel(const T* __restrict__ k,
   }
 }
 
+template <typename T, int D>
+void launch_pool_mode(dim3 grid, const T* k, const float* weights, float* kbar, bf16* pieces, int H, int B, int n,
+                      int hg, int mode, hipStream_t stream) {
+  if (mode == kPoolMax)
+    pool_keys_kernel<T, D, kPoolMax><<<grid, 256, 0, stream>>>(k, weights, kbar, pieces, H, B, n, hg);
+  else if (mode == kPoolWeighted)
+    pool_keys_kernel<T, D, kPoolWeighted><<<grid, 256, 0, stream>>>(k, weights, kbar, pieces, H, B, n, hg);
+  else
+    pool_keys_kernel<T, D, kPoolMean><<<grid, 256, 0, stream>>>(k, weights, kbar, pieces, H, B, n, hg);
+}
+
 }  // namespace
 
 hipError_t launch_pool(const void* k, bool is_f32, float* kbar, bf16* pieces, int64_t N, int H, int D, int B,
-                       hipStream_t stream) {
+                       hipStream_t stream, int mode, const float* weights) {
   const int n = static_cast<int>(N / B);
   // Heads per workgroup: the largest of 8, 4, 2, 1 that divides H (longer
   // contiguous runs per token row) while leaving at least 1024 workgroups to
@@ -120,15 +161,13 @@ hipError_t launch_pool(const void* k, bool is_f32, float* kbar, bf16* pieces, in
   while (hg > 1 && (H % hg != 0 || hg * (D / 8) > 256 || static_cast<int64_t>(n) * (H / hg) < 1024)) hg /= 2;
   dim3 grid(n, H / hg);
   if (is_f32) {
-    if (D == 128)
-      pool_keys_kernel<float, 128><<<grid, 256, 0, stream>>>(static_cast<const float*>(k), kbar, pieces, H, B, n, hg);
-    else
-      pool_keys_kernel<float, 64><<<grid, 256, 0, stream>>>(static_cast<const float*>(k), kbar, pieces, H, B, n, hg);
+    const float* kf = static_cast<const float*>(k);
+    if (D == 128) launch_pool_mode<float, 128>(grid, kf, weights, kbar, pieces, H, B, n, hg, mode, stream);
+    else launch_pool_mode<float, 64>(grid, kf, weights, kbar, pieces, H, B, n, hg, mode, stream);
   } else {
-    if (D == 128)
-      pool_keys_kernel<bf16, 128><<<grid, 256, 0, stream>>>(static_cast<const bf16*>(k), kbar, pieces, H, B, n, hg);
-    else
-      pool_keys_kernel<bf16, 64><<<grid, 256, 0, stream>>>(static_cast<const bf16*>(k), kbar, pieces, H, B, n, hg);
+    const bf16* kb = static_cast<const bf16*>(k);
+    if (D == 128) launch_pool_mode<bf16, 128>(grid, kb, weights, kbar, pieces, H, B, n, hg, mode, stream);
+    else launch_pool_mode<bf16, 64>(grid, kb, weights, kbar, pieces, H, B, n, hg, mode, stream);
   }
   return hipGetLastError();
 }

@@ -102,6 +102,53 @@ int moba_gate_topk_f32(const float* q, const float* k, int32_t* sel, int64_t N, 
                        int32_t D, int32_t block_size, int32_t topk, hipStream_t stream);
 
 /*
+ * Block pooling variants. The gate scores each past block through one
+ * representative key; the pages pool by the mean (wzjinhao.cn MoBA article,
+ * section 3, score_pooling = mean) and suggest trying max or weighted pooling
+ * instead (the same article, closing section):
+ *   MOBA_POOL_MEAN      mean of the block's keys (the default everywhere);
+ *   MOBA_POOL_MAX       per-dimension maximum over the block's keys;
+ *   MOBA_POOL_WEIGHTED  sum of w[h][t] * k[t][h][:] over the block divided by
+ *                       the sum of the weights; `weights` fp32 [H][N],
+ *                       non-negative; a block whose weights are all zero pools
+ *                       to the zero vector.
+ * The pooled key is rounded once to fp32 (max is exact; mean and weighted are
+ * summed in fp64). `weights` is read in the weighted mode only (NULL there is
+ * MOBA_ERR_INVALID_ARG; it needs 4-byte alignment); an unknown mode is
+ * MOBA_ERR_INVALID_ARG.
+ */
+#define MOBA_POOL_MEAN 0
+#define MOBA_POOL_MAX 1
+#define MOBA_POOL_WEIGHTED 2
+
+/* Pooled block keys: kbar fp32 [H][n][D] from bf16 k [N][H][D]. */
+int moba_block_pool_keys(const void* k, const float* weights, float* kbar, int64_t N, int32_t H, int32_t D,
+                         int32_t block_size, int32_t pooling, hipStream_t stream);
+
+/* moba_gate_topk, moba_prefill_fwd and moba_prefill_bwd (bf16) with the gate's
+ * block keys pooled as `pooling` says. */
+int moba_gate_topk_pooled(const void* q, const void* k, const float* weights, int32_t* sel, int64_t N, int32_t H,
+                          int32_t D, int32_t block_size, int32_t topk, int32_t pooling, hipStream_t stream);
+int moba_prefill_fwd_pooled(const void* q, const void* k, const void* v, const float* weights, void* out, float* lse,
+                            int64_t N, int32_t H, int32_t D, int32_t block_size, int32_t topk, int32_t pooling,
+                            hipStream_t stream);
+int moba_prefill_bwd_pooled(const void* q, const void* k, const void* v, const float* weights, const void* out,
+                            const float* lse, const void* dout, void* dq, void* dk, void* dv, int64_t N, int32_t H,
+                            int32_t D, int32_t block_size, int32_t topk, int32_t pooling, hipStream_t stream);
+
+/*
+ * Dynamic k (host only, no GPU work): the top_k that keeps a late query's
+ * sparsity 1 - block_size * k / N at `sparsity` for a context of N tokens,
+ * k = nearest integer to (1 - sparsity) * N / block_size (ties to even),
+ * clamped to 1 .. N / block_size. The wzjinhao.cn MoBA article lets k grow with
+ * the context (closing section); its section 3 table pairs each context length
+ * with (block_size, top_k) at about constant sparsity, which this reproduces.
+ * Returns k >= 1, or -MOBA_ERR_INVALID_ARG when N < 1, block_size < 1, N is
+ * not a multiple of block_size, or sparsity is outside [0, 1).
+ */
+int32_t moba_topk_for_sparsity(int64_t N, int32_t block_size, double sparsity);
+
+/*
  * Full MoBA causal prefill: out[t][h][:] = softmax over the attended keys of
  * q_t . k_s / sqrt(D), applied to v, where the attended keys are every key of
  * the chosen past blocks and the keys of the own block up to t itself; lse as

@@ -33,15 +33,15 @@ def to_device(x: np.ndarray, dtype: str, device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(device)
 
 
-def oracle_scores(q, k, B, rows):
+def oracle_scores(q, k, B, rows, pooling="mean", weights=None):
     """fp32 gate scores [H, R, n] from the oracle."""
     from oracle import gate_scores, pooled_keys_fp32
-    kbar32 = pooled_keys_fp32(k, B)
+    kbar32 = pooled_keys_fp32(k, B, pooling, weights)
     H = q.shape[1]
     return np.stack([gate_scores(q[rows, h, :], kbar32[h]) for h in range(H)])
 
 
-def compare_selection(gpu_sel, ref_sel, q, k, B, topk, rows=None, rel=TIE_REL):
+def compare_selection(gpu_sel, ref_sel, q, k, B, topk, rows=None, rel=TIE_REL, pooling="mean", weights=None):
     """Compare [H, R, topk] selections. Returns a dict with the number of
     mismatched rows, how many of them are exempt near-ties, and the (h, r) of
     any that are not."""
@@ -54,7 +54,7 @@ def compare_selection(gpu_sel, ref_sel, q, k, B, topk, rows=None, rel=TIE_REL):
     if diff[0].size == 0:
         return result
     sub_rows = np.unique(rows[diff[1]])
-    sc = oracle_scores(q, k, B, sub_rows)
+    sc = oracle_scores(q, k, B, sub_rows, pooling, weights)
     where = {int(t): i for i, t in enumerate(sub_rows)}
     for h, r in zip(*diff):
         t = int(rows[r])

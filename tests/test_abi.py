@@ -178,3 +178,25 @@ def test_backward_argument_checks(lib):
         ptrs = [A] * 9
         ptrs[i] = A + 4
         assert backward(lib, ptrs=tuple(ptrs)) == UNSUPPORTED, i
+
+
+def test_topk_for_sparsity_matches_oracle(lib):
+    """Host-only helper (no GPU work): the library's dynamic k equals the oracle's."""
+    from oracle import topk_for_sparsity
+    lib.moba_topk_for_sparsity.restype = ctypes.c_int32
+    lib.moba_topk_for_sparsity.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_double]
+    for N, B in [(32768, 512), (131072, 2048), (262144, 4096), (1048576, 4096), (4096, 64), (512, 512)]:
+        for s in (0.0, 0.5, 0.9, 0.906, 0.953, 0.99, 0.999):
+            assert lib.moba_topk_for_sparsity(N, B, s) == topk_for_sparsity(N, B, s), (N, B, s)
+    for args in ((0, 512, 0.9), (1000, 512, 0.9), (4096, 0, 0.9), (4096, 512, 1.0), (4096, 512, -0.1)):
+        assert lib.moba_topk_for_sparsity(*args) == -INVALID, args
+
+
+def test_pooled_argument_checks(lib):
+    f = lib.moba_gate_topk_pooled
+    assert f(A, A, None, A, 1024, 2, 128, 128, 3, 3, None) == INVALID          # unknown pooling
+    assert f(A, A, None, A, 1024, 2, 128, 128, 3, 2, None) == INVALID          # weighted without weights
+    assert f(A, A, A + 2, A, 1024, 2, 128, 128, 3, 2, None) == UNSUPPORTED     # misaligned weights
+    assert lib.moba_block_pool_keys(A, None, A, 1024, 2, 128, 128, -1, None) == INVALID
+    assert lib.moba_prefill_fwd_pooled(A, A, A, None, A, A, 1024, 2, 128, 128, 3, 2, None) == INVALID
+    assert lib.moba_prefill_bwd_pooled(A, A, A, None, A, A, A, A, A, A, 1024, 2, 128, 128, 3, 7, None) == INVALID

@@ -339,3 +339,64 @@ def test_backward_h32_one_head(moba):
         rel = float(np.linalg.norm(g - r) / np.linalg.norm(r))
         log(f"  backward h32 head {h} {name}: max|err| {err:.3e} (max|ref| {scale:.3e}), rel L2 {rel:.3e}")
         assert err <= GRAD_REL_TOL * scale and rel <= GRAD_L2_TOL, name
+
+
+POOLED = [  # (N, H, D, B, topk, pooling, seed)
+    (2048, 2, 128, 128, 3, "max", 1),
+    (2048, 2, 128, 128, 3, "weighted", 2),
+    (4096, 1, 64, 256, 4, "max", 3),
+    (4096, 2, 64, 256, 2, "weighted", 4),
+]
+
+
+@pytest.mark.parametrize("case", POOLED, ids=lambda c: "N{}_H{}_D{}_B{}_k{}_{}".format(*c[:6]))
+def test_pooling_variants(moba, case):
+    from oracle import moba_ref, pooled_keys_fp32, select_blocks
+    N, H, D, B, topk, pooling, seed = case
+    q, k, v = synth.make_qkv(N, H, D, seed=[500 + seed, 0], dtype="bf16")
+    w = np.random.default_rng([500 + seed, 1]).uniform(0.0, 1.0, (H, N)).astype(np.float32) \
+        if pooling == "weighted" else None
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    wd = torch.from_numpy(w).cuda() if w is not None else None
+    kbar = moba.block_pool_keys(kd, B, pooling, wd)
+    sel = moba.gate_topk_pooled(qd, kd, B, topk, pooling, wd)
+    out, lse = moba.prefill_pooled(qd, kd, vd, B, topk, pooling, wd)
+    torch.cuda.synchronize()
+    ref_kbar = pooled_keys_fp32(k, B, pooling, w)
+    kb = kbar.cpu().numpy()
+    if pooling == "max":
+        assert np.array_equal(kb, ref_kbar)
+    else:   # fp64 sums in another order: at most one fp32 rounding step apart
+        assert np.all(np.abs(kb - ref_kbar) <= np.spacing(np.abs(ref_kbar)))
+    gsel = sel.cpu().numpy()
+    ref_sel, _ = select_blocks(q, k, B, topk, pooling=pooling, weights=w)
+    cmp = compare_selection(gsel, ref_sel, q, k, B, topk, pooling=pooling, weights=w)
+    assert not cmp["bad"], cmp["bad"][:5]
+    ref_out, ref_lse, _ = moba_ref(q, k, v, B, topk, sel=gsel)
+    e_out = max_abs(out.float().cpu().numpy(), ref_out)
+    e_lse = max_abs(lse.cpu().numpy(), ref_lse)
+    log(f"  pooling {pooling} N={N} H={H} D={D} B={B} k={topk}: sel mismatch {cmp['mismatch']} "
+        f"(exempt {cmp['exempt']}), max|out| err {e_out:.3e}, max|lse| err {e_lse:.3e}")
+    assert e_out <= OUT_TOL["bf16"] and e_lse <= LSE_TOL["bf16"]
+    # The mean pooling differs from max pooling on these inputs: the selections are not all equal.
+    if pooling == "max":
+        assert not np.array_equal(gsel, moba.gate_topk(qd, kd, B, topk).cpu().numpy())
+
+
+def test_backward_pooled(moba):
+    """The backward pass recomputes the selection with the same pooling."""
+    from oracle import moba_backward_ref
+    N, H, D, B, topk = 1024, 2, 128, 128, 3
+    q, k, v = synth.make_qkv(N, H, D, seed=[510, 0], dtype="bf16")
+    do = synth.make_grad(N, H, D, seed=[510, 1])
+    qd, kd, vd, dod = (to_device(x, "bf16") for x in (q, k, v, do))
+    out, lse = moba.prefill_pooled(qd, kd, vd, B, topk, "max")
+    dq, dk, dv = moba.prefill_backward(qd, kd, vd, out, lse, dod, B, topk, pooling="max")
+    sel = moba.gate_topk_pooled(qd, kd, B, topk, "max")
+    torch.cuda.synchronize()
+    rq, rk, rv, _ = moba_backward_ref(q, k, v, do, B, topk, sel=sel.cpu().numpy())
+    for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        g = got.float().cpu().numpy().astype(np.float64)
+        rel = float(np.linalg.norm(g - ref) / np.linalg.norm(ref))
+        log(f"  backward max-pooled {name}: rel L2 {rel:.3e}")
+        assert rel <= GRAD_L2_TOL and float(np.max(np.abs(g - ref))) <= GRAD_REL_TOL * float(np.max(np.abs(ref)))
