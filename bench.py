@@ -12,7 +12,8 @@ library records on its stream, the roofline of the dominant kernel (the
 past-block attention launch), and the fp64 oracle timed on the host on a
 sample of query rows.
 
-A ``pooling`` object times the prefill with max and weighted block pooling.
+A ``dense`` object times the same inputs with top_k = n (every block kept:
+causal attention, counted as N(N+1)/2 pairs per head). A ``pooling`` object times the prefill with max and weighted block pooling.
 A ``backward`` object times ``moba_prefill_bwd`` (dQ, dK, dV for a seeded
 upstream gradient) on the same inputs, effective TFLOP/s counted as 2.5x the
 forward's attended-pair work. A ``decode`` object beside it times ``moba_decode_fwd`` for the newest token of
@@ -179,6 +180,28 @@ def pooling_bench(moba, w, qd, kd, vd, steps: int):
     return res
 
 
+def dense_bench(moba, w, qd, kd, vd, steps: int):
+    """top_k = n on the same inputs: every block kept, i.e. causal attention
+    over the whole sequence (the dense path; hybrid full-attention layers)."""
+    import torch
+    n = w.N // w.block_size
+    for _ in range(2):
+        moba.prefill(qd, kd, vd, w.block_size, n)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        moba.prefill(qd, kd, vd, w.block_size, n)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    flops = 4.0 * w.D * w.H * w.N * (w.N + 1) / 2
+    return {"top_k": n, "ms_per_step": ms, "causal_gflop": flops / 1e9,
+            "effective_tflops": flops / (ms * 1e-3) / 1e12,
+            "pct_peak": 100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
 def cpu_baseline(w, q, k, v, gpu_out, gpu_lse, target_s: float):
     """The fp64 oracle as it stands, on a seeded sample of query rows."""
     import threadpoolctl
@@ -227,6 +250,8 @@ def main():
     ap.add_argument("--workload", default="h32")
     ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--dense", choices=("on", "off"), default="on",
+                    help="also time the prefill with every block kept (causal attention)")
     ap.add_argument("--pooling", choices=("on", "off"), default="on",
                     help="also time the prefill with max and weighted block pooling")
     ap.add_argument("--backward", choices=("on", "off"), default="on",
@@ -351,6 +376,12 @@ def main():
         },
         "device": info,
     }
+
+    if args.dense == "on":
+        result["dense"] = dense_bench(moba, w, qd, kd, vd, max(3, args.steps // 4))
+        dn = result["dense"]
+        print(f"[bench] dense (top-k = n): {dn['ms_per_step']:.3f} ms, {dn['effective_tflops']:.1f} TFLOP/s",
+              file=sys.stderr, flush=True)
 
     if args.pooling == "on":
         result["pooling"] = pooling_bench(moba, w, qd, kd, vd, max(5, args.steps // 2))

@@ -250,9 +250,13 @@ __device__ __forceinline__ Desc item_desc(const AttnArgs<bf16>& a, int64_t idx) 
     d.count = v.w;
     d.nkt = a.B / kKTile;
   } else {
+    // Query tiles of a block in zig-zag order (first, last, second, second
+    // last, ...): the causal work of a tile grows with its position, so a
+    // workgroup's contiguous range of items mixes light and heavy tiles.
     const int per_block = (a.B + kAttnTile - 1) / kAttnTile;
     const int64_t e = idx / per_block;
-    const int qt = static_cast<int>(idx - e * per_block);
+    const int zz = static_cast<int>(idx - e * per_block);
+    const int qt = (zz & 1) ? per_block - 1 - (zz >> 1) : (zz >> 1);
     d.h = static_cast<int>(e / a.n);
     d.b = static_cast<int>(e - static_cast<int64_t>(d.h) * a.n);
     d.start = qt * kAttnTile;

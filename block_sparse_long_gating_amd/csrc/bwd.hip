@@ -154,7 +154,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
   const bool active = kofs < a.B;
   const int64_t key0 = static_cast<int64_t>(b) * a.B + kofs;
   const int64_t hb = static_cast<int64_t>(h) * a.n + b;
-  const int lstart = a.offs[hb], llen = a.totals[hb];
+  const int lstart = a.has_lists ? a.offs[hb] : 0, llen = a.has_lists ? a.totals[hb] : 0;
   const int own0 = kBwdKeys * c;                   // first own query (offset in the block) that sees the chunk
   const int t_past = (llen + kBwdQTile - 1) / kBwdQTile;
   const int t_all = t_past + (a.B - own0 + kBwdQTile - 1) / kBwdQTile;
@@ -328,8 +328,9 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
   int64_t t0 = 0;         // own items: first query
   int lstart = 0;         // past items: first list position
   if (kOwn) {
+    // Within a block, later query tiles (more keys) are dispatched first.
     const int per = (a.B + kAttnTile - 1) / kAttnTile;
-    const int x = blockIdx.x % per;
+    const int x = per - 1 - static_cast<int>(blockIdx.x % per);
     const int rest = blockIdx.x / per;
     h = rest % a.H;
     b = rest / a.H;

@@ -97,6 +97,7 @@ struct BwdArgs {
   int64_t N;
   int H, D, B, n, topk, lmax;
   int64_t max_items;
+  int has_lists;        // 0: no query lists (every block kept; one block of N tokens)
   float scale;          // 1 / sqrt(D)
   float scale_log2;     // log2(e) / sqrt(D)
 };

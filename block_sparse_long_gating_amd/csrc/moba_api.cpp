@@ -85,6 +85,12 @@ int check_shape(int64_t N, int32_t H, int32_t D, int32_t B) {
   return MOBA_OK;
 }
 
+// The dense causal path of the bf16 prefill and backward: every query keeps
+// every block (top_k >= n, n > 1).
+bool dense_path(int64_t N, int32_t B, int32_t topk, bool is_f32) {
+  return !is_f32 && N / B > 1 && topk >= N / B;
+}
+
 int check_topk(int64_t N, int32_t B, int32_t topk) {
   if (topk < 1) return MOBA_ERR_INVALID_ARG;
   const int64_t n = N / B;
@@ -263,7 +269,12 @@ int prefill_impl(const void* q, const void* k, const void* v, void* out, float* 
   if ((s = check_pooling(pl)) != MOBA_OK) return s;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
     return MOBA_ERR_UNSUPPORTED;
-  const moba::Problem p = make_problem(N, H, D, B, topk, is_f32);
+  // Every block kept (top_k >= n): the attended set of a query is every key up
+  // to itself, i.e. MoBA with one block of N tokens and top-1. That form needs
+  // no pooling, gate, query lists or partials (dense causal path).
+  const bool dense = dense_path(N, B, topk, is_f32);
+  const moba::Problem p = dense ? make_problem(N, H, D, static_cast<int32_t>(N), 1, is_f32)
+                                : make_problem(N, H, D, B, topk, is_f32);
   if (p.p_off >= (int64_t{1} << 31)) return MOBA_ERR_UNSUPPORTED;
   DeviceState* st = nullptr;
   if ((s = current_device(&st)) != MOBA_OK) return s;
@@ -273,12 +284,12 @@ int prefill_impl(const void* q, const void* k, const void* v, void* out, float* 
   moba::Workspace ws = bind(w, base, true);
   auto mark = [&](int i) { return events && events[i] ? hipEventRecord(events[i], stream) : hipSuccess; };
   hipError_t e = mark(0);
-  if (e == hipSuccess)
+  if (e == hipSuccess && !dense)
     e = moba::launch_pool(k, is_f32, ws.kbar, is_f32 ? nullptr : ws.kpieces, N, H, D, B, stream, pl.mode, pl.weights);
   if (e == hipSuccess) e = mark(1);
-  if (e == hipSuccess) e = moba::launch_gate(p, q, ws, ws.sel, true, st->num_cus, stream);
+  if (e == hipSuccess && !dense) e = moba::launch_gate(p, q, ws, ws.sel, true, st->num_cus, stream);
   if (e == hipSuccess) e = mark(2);
-  if (e == hipSuccess) e = moba::launch_csr(p, ws, ws.sel, stream);
+  if (e == hipSuccess && !dense) e = moba::launch_csr(p, ws, ws.sel, stream);
   if (e == hipSuccess) e = mark(3);
   if (e == hipSuccess) e = moba::launch_attention(p, q, k, v, ws, out, lse, st->num_cus, stream, mark);
   if (e == hipSuccess) e = mark(5);
@@ -300,7 +311,9 @@ int backward_impl(const void* q, const void* k, const void* v, const void* out, 
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse) || !aligned16(dout) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return MOBA_ERR_UNSUPPORTED;
-  const moba::Problem p = make_problem(N, H, D, B, topk, false);
+  const bool dense = dense_path(N, B, topk, false);   // see prefill_impl
+  const moba::Problem p = dense ? make_problem(N, H, D, static_cast<int32_t>(N), 1, false)
+                                : make_problem(N, H, D, B, topk, false);
   if (p.p_off >= (int64_t{1} << 31)) return MOBA_ERR_UNSUPPORTED;
   DeviceState* st = nullptr;
   if ((s = current_device(&st)) != MOBA_OK) return s;
@@ -330,16 +343,20 @@ int backward_impl(const void* q, const void* k, const void* v, const void* out, 
   a.N = N;
   a.H = H;
   a.D = D;
-  a.B = B;
+  a.B = p.B;
   a.n = p.n;
-  a.topk = topk;
+  a.topk = p.topk;
   a.lmax = p.lmax;
   a.max_items = p.lmax > 0 ? p.max_items : 0;
+  a.has_lists = dense ? 0 : 1;
   a.scale = 1.0f / std::sqrt(static_cast<float>(D));
   a.scale_log2 = 1.4426950408889634f / std::sqrt(static_cast<float>(D));
-  hipError_t e = moba::launch_pool(k, false, ws.kbar, ws.kpieces, N, H, D, B, stream, pl.mode, pl.weights);
-  if (e == hipSuccess) e = moba::launch_gate(p, q, ws, ws.sel, true, st->num_cus, stream);
-  if (e == hipSuccess) e = moba::launch_csr(p, ws, ws.sel, stream);
+  hipError_t e = hipSuccess;
+  if (!dense) {
+    e = moba::launch_pool(k, false, ws.kbar, ws.kpieces, N, H, D, B, stream, pl.mode, pl.weights);
+    if (e == hipSuccess) e = moba::launch_gate(p, q, ws, ws.sel, true, st->num_cus, stream);
+    if (e == hipSuccess) e = moba::launch_csr(p, ws, ws.sel, stream);
+  }
   if (e == hipSuccess) e = moba::launch_backward(a, stream);
   return finish(e, base, stream);
 }
