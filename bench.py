@@ -13,7 +13,8 @@ past-block attention launch), and the fp64 oracle timed on the host on a
 sample of query rows.
 
 A ``dense`` object times the same inputs with top_k = n (every block kept:
-causal attention, counted as N(N+1)/2 pairs per head). A ``pooling`` object times the prefill with max and weighted block pooling.
+causal attention, counted as N(N+1)/2 pairs per head). A ``varlen`` object times the same tokens as 8 packed sequences of N/8 tokens.
+A ``pooling`` object times the prefill with max and weighted block pooling.
 A ``backward`` object times ``moba_prefill_bwd`` (dQ, dK, dV for a seeded
 upstream gradient) on the same inputs, effective TFLOP/s counted as 2.5x the
 forward's attended-pair work. A ``decode`` object beside it times ``moba_decode_fwd`` for the newest token of
@@ -202,6 +203,27 @@ def dense_bench(moba, w, qd, kd, vd, steps: int):
             "pct_peak": 100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
+def varlen_bench(moba, w, qd, kd, vd, steps: int, nseq: int = 8):
+    """The same tokens as ``nseq`` packed sequences of N / nseq tokens each."""
+    import torch
+    L = w.N // nseq
+    cu = [i * L for i in range(nseq + 1)]
+    for _ in range(2):
+        moba.prefill_varlen(qd, kd, vd, cu, w.block_size, w.topk)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        moba.prefill_varlen(qd, kd, vd, cu, w.block_size, w.topk)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    flops = 4.0 * w.D * w.H * nseq * effective_pairs(L, w.block_size, w.topk)
+    return {"sequences": nseq, "tokens_each": L, "ms_per_step": ms, "effective_gflop": flops / 1e9,
+            "effective_tflops": flops / (ms * 1e-3) / 1e12}
+
+
 def cpu_baseline(w, q, k, v, gpu_out, gpu_lse, target_s: float):
     """The fp64 oracle as it stands, on a seeded sample of query rows."""
     import threadpoolctl
@@ -252,6 +274,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--dense", choices=("on", "off"), default="on",
                     help="also time the prefill with every block kept (causal attention)")
+    ap.add_argument("--varlen", choices=("on", "off"), default="on",
+                    help="also time the same tokens as 8 packed sequences")
     ap.add_argument("--pooling", choices=("on", "off"), default="on",
                     help="also time the prefill with max and weighted block pooling")
     ap.add_argument("--backward", choices=("on", "off"), default="on",
@@ -382,6 +406,12 @@ def main():
         dn = result["dense"]
         print(f"[bench] dense (top-k = n): {dn['ms_per_step']:.3f} ms, {dn['effective_tflops']:.1f} TFLOP/s",
               file=sys.stderr, flush=True)
+
+    if args.varlen == "on":
+        result["varlen"] = varlen_bench(moba, w, qd, kd, vd, max(5, args.steps // 2))
+        vl = result["varlen"]
+        print(f"[bench] varlen ({vl['sequences']} x {vl['tokens_each']}): {vl['ms_per_step']:.3f} ms, "
+              f"{vl['effective_tflops']:.1f} effective TFLOP/s", file=sys.stderr, flush=True)
 
     if args.pooling == "on":
         result["pooling"] = pooling_bench(moba, w, qd, kd, vd, max(5, args.steps // 2))

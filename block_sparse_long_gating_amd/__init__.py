@@ -45,6 +45,9 @@ _SIGNATURES = {
     "moba_prefill_fwd_pooled": [_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _P],
     "moba_prefill_bwd_pooled": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _P],
     "moba_topk_for_sparsity": [_I64, _I32, ctypes.c_double],
+    "moba_gate_topk_varlen": [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P],
+    "moba_prefill_fwd_varlen": [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P],
+    "moba_prefill_bwd_varlen": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P],
     "moba_status_string": [ctypes.c_int],
     "moba_last_hip_error": [],
 }
@@ -275,6 +278,65 @@ def prefill_pooled(q, k, v, block_size: int, topk: int, pooling: str = "mean", w
     _check(lib.moba_prefill_fwd_pooled(q.data_ptr(), k.data_ptr(), v.data_ptr(), wp, out.data_ptr(), lse.data_ptr(),
                                        N, H, D, block_size, topk, mode, _stream(q.device)), "moba_prefill_fwd_pooled")
     return out, lse
+
+
+def _cu(cu_seqlens):
+    """Host int64 copy of cu_seqlens (a list, numpy array or CPU tensor) and its ctypes pointer."""
+    import numpy as np
+    arr = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    if arr.ndim != 1 or arr.size < 2:
+        raise ValueError("cu_seqlens must hold num_seqs + 1 offsets")
+    return arr, arr.ctypes.data_as(ctypes.c_void_p), arr.size - 1
+
+
+def gate_topk_varlen(q, k, cu_seqlens, block_size: int, topk: int):
+    """Selections of packed sequences (bf16): int32 ``[H, T, topk]``, global block indices."""
+    import torch
+    T, H, D, f32 = _check_qkv(q, k)
+    if f32:
+        raise TypeError("packed sequences take bf16 tensors")
+    arr, cp, S = _cu(cu_seqlens)
+    lib = load_library()
+    sel = torch.empty((H, T, max(topk, 1)), dtype=torch.int32, device=q.device)
+    _check(lib.moba_gate_topk_varlen(q.data_ptr(), k.data_ptr(), sel.data_ptr(), cp, S, H, D, block_size, topk,
+                                     _stream(q.device)), "moba_gate_topk_varlen")
+    return sel
+
+
+def prefill_varlen(q, k, v, cu_seqlens, block_size: int, topk: int, out=None, lse=None):
+    """MoBA prefill of packed sequences (bf16 ``[T, H, D]``): ``(out, lse [H, T])``."""
+    import torch
+    T, H, D, f32 = _check_qkv(q, k, v)
+    if f32:
+        raise TypeError("packed sequences take bf16 tensors")
+    arr, cp, S = _cu(cu_seqlens)
+    lib = load_library()
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if lse is None else lse
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (H, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [H, T] tensor")
+    _check(lib.moba_prefill_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), cp,
+                                       S, H, D, block_size, topk, _stream(q.device)), "moba_prefill_fwd_varlen")
+    return out, lse
+
+
+def prefill_backward_varlen(q, k, v, out, lse, dout, cu_seqlens, block_size: int, topk: int):
+    """Gradients of :func:`prefill_varlen`: ``(dq, dk, dv)`` bf16 ``[T, H, D]``."""
+    import torch
+    T, H, D, f32 = _check_qkv(q, k, v, out, dout)
+    if f32:
+        raise TypeError("packed sequences take bf16 tensors")
+    if lse.shape != (H, T) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous fp32 [H, T] tensor on q's device")
+    arr, cp, S = _cu(cu_seqlens)
+    lib = load_library()
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    _check(lib.moba_prefill_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                       dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cp, S, H, D,
+                                       block_size, topk, _stream(q.device)), "moba_prefill_bwd_varlen")
+    return dq, dk, dv
 
 
 def topk_for_sparsity(N: int, block_size: int, sparsity: float) -> int:

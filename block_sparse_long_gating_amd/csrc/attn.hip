@@ -56,6 +56,7 @@ struct AttnArgs {
   int64_t p_off;        // past-block list entries (rows of part_off before the dump rows)
   int64_t own_items;    // own-block items of the MFMA kernel: H * n * ceil(B / kAttnTile)
   int topk, lmax;
+  const int32_t* blo;   // first block of each block's sequence (packed sequences) or nullptr
   T* out;               // final output [N][H][D] (own-block kernel with the merge fused in)
   float* lse_out;       // final lse [H][N]
   float scale_log2;     // log2(e) / sqrt(D)
@@ -262,7 +263,15 @@ __device__ __forceinline__ Desc item_desc(const AttnArgs<bf16>& a, int64_t idx) 
     d.start = qt * kAttnTile;
     d.count = min(kAttnTile, a.B - d.start);
     d.nkt = (d.start + d.count) / kKTile;
-    if (kFused) d.np = 2 * min(a.topk - 1, d.b);
+    if (kFused) {
+      int lo = 0;
+      if (a.blo != nullptr) {
+        // Scalar load, waited for in the same statement (written by an earlier kernel).
+        const uint64_t addr = uniform_ptr(a.blo + uniform_u32(d.b));
+        asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(lo) : "s"(addr));
+      }
+      d.np = 2 * kept_past(d.b, lo, a.topk);
+    }
   }
   d.h = static_cast<int>(uniform_u32(d.h));
   d.b = static_cast<int>(uniform_u32(d.b));
@@ -1053,6 +1062,7 @@ AttnArgs<T> make_args(const Problem& p, const void* q, const void* k, const void
   a.own_items = static_cast<int64_t>(p.H) * p.n * ((p.B + kAttnTile - 1) / kAttnTile);
   a.topk = p.topk;
   a.lmax = p.lmax;
+  a.blo = p.blo;
   a.out = nullptr;
   a.lse_out = nullptr;
   a.scale_log2 = kLog2e / sqrtf(static_cast<float>(p.D));

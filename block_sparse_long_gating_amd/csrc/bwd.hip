@@ -445,7 +445,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
   }
   // Own block: add the query's past partials, scale, write dQ.
   const int j = b;
-  const int np = min(j, a.topk - 1);
+  const int np = kept_past(j, a.blo != nullptr ? a.blo[j] : 0, a.topk);
   const int64_t ibase = (static_cast<int64_t>(h) * a.N + t) * a.lmax;
   for (int s2 = 0; s2 < np; ++s2) {
     const float* src = a.part_dq + static_cast<int64_t>(a.inv[ibase + s2]) * D;

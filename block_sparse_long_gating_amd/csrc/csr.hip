@@ -93,13 +93,13 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
                                                       const int32_t* __restrict__ cnt,
                                                       const int32_t* __restrict__ offs, int32_t* __restrict__ qidx,
                                                       int32_t* __restrict__ inv, int64_t N, int H, int B, int n,
-                                                      int topk, int lmax, int ntiles) {
+                                                      int topk, int lmax, int ntiles, const int32_t* __restrict__ blo) {
   const int64_t g = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (g >= N * H) return;
   const int h = static_cast<int>(g / N);
   const int64_t t = g % N;
   const int j = static_cast<int>(t / B);
-  const int L = j < topk - 1 ? j : topk - 1;   // kept past blocks, in ascending order in sel
+  const int L = kept_past(j, blo != nullptr ? blo[j] : 0, topk);   // kept past blocks, ascending in sel
   const int tile = static_cast<int>(t / kQTile);
   const int32_t* srow = sel + g * topk;
   const int32_t* rrow = rk + g * lmax;
@@ -122,7 +122,30 @@ hipError_t launch_csr(const Problem& p, const Workspace& ws, const int32_t* sel,
   const int64_t threads = p.N * p.H;
   if (p.lmax > 0)
     scatter_kernel<<<static_cast<unsigned>((threads + 255) / 256), 256, 0, stream>>>(
-        sel, ws.rk, ws.cnt, ws.offs, ws.qidx, ws.inv, p.N, p.H, p.B, p.n, p.topk, p.lmax, p.ntiles);
+        sel, ws.rk, ws.cnt, ws.offs, ws.qidx, ws.inv, p.N, p.H, p.B, p.n, p.topk, p.lmax, p.ntiles, p.blo);
+  return hipGetLastError();
+}
+
+namespace {
+
+__global__ __launch_bounds__(256) void seq_lo_kernel(SeqStarts st, int32_t* __restrict__ blo, int n) {
+  const int j = static_cast<int>(blockIdx.x) * 256 + threadIdx.x;
+  if (j >= n) return;
+  // The last sequence whose first block is <= j (empty sequences share their
+  // start with the next one, so the last such sequence is the one holding j).
+  int lo = 0, hi = st.nseq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (st.start[mid] <= j) lo = mid;
+    else hi = mid - 1;
+  }
+  blo[j] = st.start[lo];
+}
+
+}  // namespace
+
+hipError_t launch_seq_lo(const SeqStarts& st, int32_t* blo, int n, hipStream_t stream) {
+  seq_lo_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, stream>>>(st, blo, n);
   return hipGetLastError();
 }
 

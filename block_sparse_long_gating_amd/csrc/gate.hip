@@ -42,6 +42,7 @@ struct GateArgs {
   int32_t* rk;
   int64_t N;
   int H, B, n, topk, lmax, ntiles;
+  const int32_t* blo;   // first block of each block's sequence (packed sequences) or nullptr
 };
 
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
@@ -100,14 +101,14 @@ __device__ __forceinline__ void merge_with_partner(uint64_t (&list)[KCAP]) {
 // list bookkeeping. Called by all 256 threads of the workgroup (it has barriers).
 template <int KCAP>
 __device__ __forceinline__ void finalize(const GateArgs& a, const uint64_t (&list)[KCAP], int64_t t, bool valid,
-                                         int j, uint32_t* bm, int tile) {
+                                         int j, int lo, uint32_t* bm, int tile) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int qn = lane & 31;
   const int half = lane >> 5;
   const int h = blockIdx.y;
   const int topk = a.topk;
-  const bool ranked = j >= topk;   // more past blocks than slots: the gate decides
+  const bool ranked = j - lo >= topk;   // more eligible past blocks than slots: the gate decides
   const int nk = topk - 1;         // past blocks kept when ranked
 
   // Position of each kept past block in ascending block order.
@@ -124,7 +125,7 @@ __device__ __forceinline__ void finalize(const GateArgs& a, const uint64_t (&lis
   if (valid && half == 0) {
     int32_t* srow = a.sel + (static_cast<int64_t>(h) * a.N + t) * topk;
     if (!ranked) {
-      for (int s = 0; s < topk; ++s) srow[s] = s <= j ? s : -1;
+      for (int s = 0; s < topk; ++s) srow[s] = lo + s <= j ? lo + s : -1;
     } else {
 #pragma unroll
       for (int s = 0; s < KCAP; ++s)
@@ -142,7 +143,7 @@ __device__ __forceinline__ void finalize(const GateArgs& a, const uint64_t (&lis
     uint32_t* mine = bm + w * n;
     const uint32_t bit = 1u << qn;
     if (!ranked) {
-      for (int b = 0; b < j; ++b) atomicOr(mine + b, bit);
+      for (int b = lo; b < j; ++b) atomicOr(mine + b, bit);
     } else {
 #pragma unroll
       for (int s = 0; s < KCAP; ++s)
@@ -163,7 +164,7 @@ __device__ __forceinline__ void finalize(const GateArgs& a, const uint64_t (&lis
       return r;
     };
     if (!ranked) {
-      for (int b = 0; b < j; ++b) rrow[b] = rank_of(b);
+      for (int b = lo; b < j; ++b) rrow[b - lo] = rank_of(b);
     } else {
 #pragma unroll
       for (int s = 0; s < KCAP; ++s)
@@ -221,6 +222,7 @@ __global__ __launch_bounds__(256) void gate_mfma_kernel(const bf16* __restrict__
     const bool valid = t < a.N;
     const int64_t tc = valid ? t : a.N - 1;
     const int j = static_cast<int>(tc / a.B);
+    const int lo = a.blo != nullptr ? a.blo[j] : 0;   // first block of the query's sequence
     const int64_t tlast = (t0w + 31 < a.N) ? t0w + 31 : a.N - 1;
     const int jw = static_cast<int>(tlast / a.B);   // largest block of the wave
     // Next tile's queries, in flight while this tile is scored.
@@ -252,13 +254,13 @@ __global__ __launch_bounds__(256) void gate_mfma_kernel(const bf16* __restrict__
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int b = bc * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          sl.push(b < j ? acc[r] : -INFINITY, b);
+          sl.push(b < j && b >= lo ? acc[r] : -INFINITY, b);
         }
       }
       sl.to_keys(list);
       merge_with_partner<KCAP>(list);
     }
-    finalize<KCAP>(a, list, t, valid, j, bmb + buf * 4 * n, tile);
+    finalize<KCAP>(a, list, t, valid, j, lo, bmb + buf * 4 * n, tile);
     if (two_bm) buf ^= 1;
     else if (a.cnt != nullptr) __syncthreads();
 #pragma unroll
@@ -280,6 +282,7 @@ __global__ __launch_bounds__(256) void gate_f32_kernel(const float* __restrict__
   const bool valid = t < a.N;
   const int64_t tc = valid ? t : a.N - 1;
   const int j = static_cast<int>(tc / a.B);
+  const int lo = a.blo != nullptr ? a.blo[j] : 0;
   const int64_t tlast = (t0w + 31 < a.N) ? t0w + 31 : a.N - 1;
   const int jw = static_cast<int>(tlast / a.B);
 
@@ -300,11 +303,11 @@ __global__ __launch_bounds__(256) void gate_f32_kernel(const float* __restrict__
       float s = 0.f;
 #pragma unroll
       for (int d = 0; d < D; ++d) s = fmaf(qr[d], kb[d], s);
-      topk_insert<KCAP>(list, b < j ? rank_key(s, b) : 0ull);
+      topk_insert<KCAP>(list, b < j && b >= lo ? rank_key(s, b) : 0ull);
     }
     merge_with_partner<KCAP>(list);
   }
-  finalize<KCAP>(a, list, t, valid, j, bm, blockIdx.x);
+  finalize<KCAP>(a, list, t, valid, j, lo, bm, blockIdx.x);
 }
 
 template <int D, int KCAP>
@@ -321,6 +324,7 @@ hipError_t launch_gate_t(const Problem& p, const void* q, const Workspace& ws, i
   a.topk = p.topk;
   a.lmax = p.lmax;
   a.ntiles = p.ntiles;
+  a.blo = p.blo;
   if (p.is_f32) {
     dim3 grid(p.ntiles, p.H);
     const size_t smem = csr ? static_cast<size_t>(4) * p.n * sizeof(uint32_t) : 0;

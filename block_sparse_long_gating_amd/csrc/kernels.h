@@ -21,7 +21,23 @@ struct Problem {
   int64_t max_items;   // upper bound on off-diagonal work items
   int64_t diag_items;  // own-block work items: H * n * ceil(B / kAttnTile)
   bool is_f32;
+  // Several sequences packed along N (each a whole number of blocks): blo[j]
+  // is the first block of block j's sequence, the lowest block its queries may
+  // select. nullptr: one sequence (blo[j] = 0).
+  const int32_t* blo = nullptr;
 };
+
+// Past blocks a query of block j keeps: min(topk - 1, j - lo) with lo the first
+// block of its sequence.
+__host__ __device__ inline int kept_past(int j, int lo, int topk) { return j - lo < topk - 1 ? j - lo : topk - 1; }
+
+// Sequence starts in block units for the blo table (at most kMaxSeqs sequences).
+constexpr int kMaxSeqs = 512;
+struct SeqStarts {
+  int32_t nseq;
+  int32_t start[kMaxSeqs + 1];   // start[s] = first block of sequence s; start[nseq] = n
+};
+hipError_t launch_seq_lo(const SeqStarts& st, int32_t* blo, int n, hipStream_t stream);
 
 // Block pooling modes (MOBA_POOL_* in moba.h).
 constexpr int kPoolMean = 0, kPoolMax = 1, kPoolWeighted = 2;
@@ -98,6 +114,7 @@ struct BwdArgs {
   int H, D, B, n, topk, lmax;
   int64_t max_items;
   int has_lists;        // 0: no query lists (every block kept; one block of N tokens)
+  const int32_t* blo;   // per-block first block of its sequence (packed sequences), or nullptr
   float scale;          // 1 / sqrt(D)
   float scale_log2;     // log2(e) / sqrt(D)
 };

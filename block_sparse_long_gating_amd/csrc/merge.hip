@@ -64,6 +64,7 @@ struct MergeArgs {
   float* lse;
   int64_t N;
   int H, B, topk, lmax;
+  const int32_t* blo;
 };
 
 template <typename T, int D>
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs<T> a) {
   const int64_t t = g / a.H;
   const int h = static_cast<int>(g % a.H);
   const int j = static_cast<int>(t / a.B);
-  const int L = j < a.topk - 1 ? j : a.topk - 1;
+  const int L = kept_past(j, a.blo != nullptr ? a.blo[j] : 0, a.topk);
   const int64_t dr = static_cast<int64_t>(h) * a.N + t;
   const int32_t* irow = a.inv + dr * a.lmax;
 
@@ -119,6 +120,7 @@ hipError_t launch_merge_t(const Problem& p, const Workspace& ws, void* out, floa
   a.B = p.B;
   a.topk = p.topk;
   a.lmax = p.lmax;
+  a.blo = p.blo;
   const int64_t threads = p.N * p.H * (D / 8);
   merge_kernel<T, D><<<static_cast<unsigned>((threads + 255) / 256), 256, 0, stream>>>(a);
   return hipGetLastError();

@@ -129,13 +129,13 @@ struct Layout {
 // Workspace offsets for the requested stages.
 struct WsPlan {
   size_t kbar, kpieces, cnt, totals, offs, rk, qidx, inv, items, counters, part_diag, lse_diag, part_off, lse_off,
-      sel, delta, part_dq;
+      sel, delta, part_dq, blo;
   size_t total;
 };
 
 // `full`: the query lists and the forward partials; `backward`: the query
 // lists and the backward's Δ and dQ partials instead of the forward partials.
-WsPlan plan(const moba::Problem& p, bool full, bool backward = false) {
+WsPlan plan(const moba::Problem& p, bool full, bool backward = false, bool packed = false) {
   Layout L;
   WsPlan w;
   std::memset(&w, 0, sizeof(w));
@@ -164,6 +164,7 @@ WsPlan plan(const moba::Problem& p, bool full, bool backward = false) {
     }
     w.sel = L.add(hN * p.topk * 4);
   }
+  if (packed) w.blo = L.add(static_cast<size_t>(p.n) * 4);
   w.total = L.total;
   return w;
 }
@@ -225,6 +226,46 @@ int check_pooling(const Pooling& pl) {
   return MOBA_OK;
 }
 
+// Several sequences packed along N, each a whole number of blocks.
+struct Packed {
+  moba::SeqStarts st;          // block-unit starts (passed by value to the table kernel)
+  int max_blocks = 0;          // blocks of the longest sequence
+  int64_t pairs_per_head = 0;  // sum over sequences and their blocks jj of B * min(topk - 1, jj)
+};
+
+// Validates the host array cu_seqlens[0..num_seqs] (token offsets: 0, then
+// non-decreasing, every length a multiple of B) and fills `pk` and the total
+// token count.
+int parse_packed(const int64_t* cu, int32_t num_seqs, int32_t B, int32_t topk, Packed* pk, int64_t* total) {
+  if (cu == nullptr || num_seqs < 1 || B < 1 || topk < 1) return MOBA_ERR_INVALID_ARG;
+  if (num_seqs > moba::kMaxSeqs) return MOBA_ERR_UNSUPPORTED;
+  if (cu[0] != 0) return MOBA_ERR_INVALID_ARG;
+  pk->st.nseq = num_seqs;
+  pk->max_blocks = 0;
+  pk->pairs_per_head = 0;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int64_t len = cu[s + 1] - cu[s];
+    if (len < 0 || len % B != 0) return MOBA_ERR_INVALID_ARG;
+    if (cu[s + 1] >= (int64_t{1} << 28)) return MOBA_ERR_UNSUPPORTED;
+    const int nb = static_cast<int>(len / B);
+    pk->st.start[s] = static_cast<int32_t>(cu[s] / B);
+    pk->max_blocks = std::max(pk->max_blocks, nb);
+    for (int jj = 0; jj < nb; ++jj) pk->pairs_per_head += static_cast<int64_t>(B) * std::min(topk - 1, jj);
+  }
+  pk->st.start[num_seqs] = static_cast<int32_t>(cu[num_seqs] / B);
+  *total = cu[num_seqs];
+  if (*total < 1) return MOBA_ERR_INVALID_ARG;
+  if (topk > MOBA_MAX_TOPK && topk < pk->max_blocks) return MOBA_ERR_UNSUPPORTED;
+  return MOBA_OK;
+}
+
+// The problem of packed sequences: list sizes from the sequences' own blocks.
+void apply_packed(const Packed& pk, moba::Problem* p) {
+  p->p_off = pk.pairs_per_head * p->H;
+  p->lmax = std::max(0, std::min(p->topk - 1, pk.max_blocks - 1));
+  p->max_items = p->p_off / moba::kAttnTile + static_cast<int64_t>(p->H) * p->n;
+}
+
 int block_mean_keys_impl(const void* k, float* kbar, int64_t N, int32_t H, int32_t D, int32_t B, hipStream_t stream,
                          bool is_f32, const Pooling& pl = Pooling()) {
   if (k == nullptr || kbar == nullptr) return MOBA_ERR_INVALID_ARG;
@@ -239,51 +280,64 @@ int block_mean_keys_impl(const void* k, float* kbar, int64_t N, int32_t H, int32
 }
 
 int gate_impl(const void* q, const void* k, int32_t* sel, int64_t N, int32_t H, int32_t D, int32_t B, int32_t topk,
-              hipStream_t stream, bool is_f32, const Pooling& pl = Pooling()) {
+              hipStream_t stream, bool is_f32, const Pooling& pl = Pooling(), const Packed* pk = nullptr) {
   if (q == nullptr || k == nullptr || sel == nullptr) return MOBA_ERR_INVALID_ARG;
   int s = check_shape(N, H, D, B);
   if (s != MOBA_OK) return s;
-  if ((s = check_topk(N, B, topk)) != MOBA_OK) return s;
+  if (pk == nullptr && (s = check_topk(N, B, topk)) != MOBA_OK) return s;
   if ((s = check_pooling(pl)) != MOBA_OK) return s;
   if (!aligned16(q) || !aligned16(k) || !aligned16(sel)) return MOBA_ERR_UNSUPPORTED;
   DeviceState* st = nullptr;
   if ((s = current_device(&st)) != MOBA_OK) return s;
-  const moba::Problem p = make_problem(N, H, D, B, topk, is_f32);
-  const WsPlan w = plan(p, false);
+  moba::Problem p = make_problem(N, H, D, B, topk, is_f32);
+  if (pk != nullptr) apply_packed(*pk, &p);
+  const WsPlan w = plan(p, false, false, pk != nullptr);
   char* base = nullptr;
   if ((s = alloc_ws(st, w.total, stream, &base)) != MOBA_OK) return s;
   moba::Workspace ws = bind(w, base, false);
-  hipError_t e =
-      moba::launch_pool(k, is_f32, ws.kbar, is_f32 ? nullptr : ws.kpieces, N, H, D, B, stream, pl.mode, pl.weights);
+  hipError_t e = hipSuccess;
+  if (pk != nullptr) {
+    int32_t* blo = reinterpret_cast<int32_t*>(base + w.blo);
+    p.blo = blo;
+    e = moba::launch_seq_lo(pk->st, blo, p.n, stream);
+  }
+  if (e == hipSuccess)
+    e = moba::launch_pool(k, is_f32, ws.kbar, is_f32 ? nullptr : ws.kpieces, N, H, D, B, stream, pl.mode, pl.weights);
   if (e == hipSuccess) e = moba::launch_gate(p, q, ws, sel, false, st->num_cus, stream);
   return finish(e, base, stream);
 }
 
 int prefill_impl(const void* q, const void* k, const void* v, void* out, float* lse, int64_t N, int32_t H, int32_t D,
                  int32_t B, int32_t topk, hipStream_t stream, bool is_f32, hipEvent_t* events = nullptr,
-                 const Pooling& pl = Pooling()) {
+                 const Pooling& pl = Pooling(), const Packed* pk = nullptr) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || lse == nullptr) return MOBA_ERR_INVALID_ARG;
   int s = check_shape(N, H, D, B);
   if (s != MOBA_OK) return s;
-  if ((s = check_topk(N, B, topk)) != MOBA_OK) return s;
+  if (pk == nullptr && (s = check_topk(N, B, topk)) != MOBA_OK) return s;
   if ((s = check_pooling(pl)) != MOBA_OK) return s;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
     return MOBA_ERR_UNSUPPORTED;
   // Every block kept (top_k >= n): the attended set of a query is every key up
   // to itself, i.e. MoBA with one block of N tokens and top-1. That form needs
   // no pooling, gate, query lists or partials (dense causal path).
-  const bool dense = dense_path(N, B, topk, is_f32);
-  const moba::Problem p = dense ? make_problem(N, H, D, static_cast<int32_t>(N), 1, is_f32)
-                                : make_problem(N, H, D, B, topk, is_f32);
+  const bool dense = pk == nullptr && dense_path(N, B, topk, is_f32);
+  moba::Problem p = dense ? make_problem(N, H, D, static_cast<int32_t>(N), 1, is_f32)
+                          : make_problem(N, H, D, B, topk, is_f32);
+  if (pk != nullptr) apply_packed(*pk, &p);
   if (p.p_off >= (int64_t{1} << 31)) return MOBA_ERR_UNSUPPORTED;
   DeviceState* st = nullptr;
   if ((s = current_device(&st)) != MOBA_OK) return s;
-  const WsPlan w = plan(p, true);
+  const WsPlan w = plan(p, true, false, pk != nullptr);
   char* base = nullptr;
   if ((s = alloc_ws(st, w.total, stream, &base)) != MOBA_OK) return s;
   moba::Workspace ws = bind(w, base, true);
   auto mark = [&](int i) { return events && events[i] ? hipEventRecord(events[i], stream) : hipSuccess; };
   hipError_t e = mark(0);
+  if (e == hipSuccess && pk != nullptr) {
+    int32_t* blo = reinterpret_cast<int32_t*>(base + w.blo);
+    p.blo = blo;
+    e = moba::launch_seq_lo(pk->st, blo, p.n, stream);
+  }
   if (e == hipSuccess && !dense)
     e = moba::launch_pool(k, is_f32, ws.kbar, is_f32 ? nullptr : ws.kpieces, N, H, D, B, stream, pl.mode, pl.weights);
   if (e == hipSuccess) e = mark(1);
@@ -300,24 +354,25 @@ int prefill_impl(const void* q, const void* k, const void* v, void* out, float* 
 
 int backward_impl(const void* q, const void* k, const void* v, const void* out, const float* lse, const void* dout,
                   void* dq, void* dk, void* dv, int64_t N, int32_t H, int32_t D, int32_t B, int32_t topk,
-                  hipStream_t stream, const Pooling& pl = Pooling()) {
+                  hipStream_t stream, const Pooling& pl = Pooling(), const Packed* pk = nullptr) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || lse == nullptr || dout == nullptr ||
       dq == nullptr || dk == nullptr || dv == nullptr)
     return MOBA_ERR_INVALID_ARG;
   int s = check_shape(N, H, D, B);
   if (s != MOBA_OK) return s;
-  if ((s = check_topk(N, B, topk)) != MOBA_OK) return s;
+  if (pk == nullptr && (s = check_topk(N, B, topk)) != MOBA_OK) return s;
   if ((s = check_pooling(pl)) != MOBA_OK) return s;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse) || !aligned16(dout) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return MOBA_ERR_UNSUPPORTED;
-  const bool dense = dense_path(N, B, topk, false);   // see prefill_impl
-  const moba::Problem p = dense ? make_problem(N, H, D, static_cast<int32_t>(N), 1, false)
-                                : make_problem(N, H, D, B, topk, false);
+  const bool dense = pk == nullptr && dense_path(N, B, topk, false);   // see prefill_impl
+  moba::Problem p = dense ? make_problem(N, H, D, static_cast<int32_t>(N), 1, false)
+                          : make_problem(N, H, D, B, topk, false);
+  if (pk != nullptr) apply_packed(*pk, &p);
   if (p.p_off >= (int64_t{1} << 31)) return MOBA_ERR_UNSUPPORTED;
   DeviceState* st = nullptr;
   if ((s = current_device(&st)) != MOBA_OK) return s;
-  const WsPlan w = plan(p, true, true);
+  const WsPlan w = plan(p, true, true, pk != nullptr);
   char* base = nullptr;
   if ((s = alloc_ws(st, w.total, stream, &base)) != MOBA_OK) return s;
   moba::Workspace ws = bind(w, base, true);
@@ -352,7 +407,13 @@ int backward_impl(const void* q, const void* k, const void* v, const void* out, 
   a.scale = 1.0f / std::sqrt(static_cast<float>(D));
   a.scale_log2 = 1.4426950408889634f / std::sqrt(static_cast<float>(D));
   hipError_t e = hipSuccess;
-  if (!dense) {
+  if (pk != nullptr) {
+    int32_t* blo = reinterpret_cast<int32_t*>(base + w.blo);
+    p.blo = blo;
+    a.blo = blo;
+    e = moba::launch_seq_lo(pk->st, blo, p.n, stream);
+  }
+  if (!dense && e == hipSuccess) {
     e = moba::launch_pool(k, false, ws.kbar, ws.kpieces, N, H, D, B, stream, pl.mode, pl.weights);
     if (e == hipSuccess) e = moba::launch_gate(p, q, ws, ws.sel, true, st->num_cus, stream);
     if (e == hipSuccess) e = moba::launch_csr(p, ws, ws.sel, stream);
@@ -507,6 +568,36 @@ int moba_prefill_bwd_pooled(const void* q, const void* k, const void* v, const f
   pl.mode = pooling;
   pl.weights = weights;
   return backward_impl(q, k, v, out, lse, dout, dq, dk, dv, N, H, D, block_size, topk, stream, pl);
+}
+
+int moba_gate_topk_varlen(const void* q, const void* k, int32_t* sel, const int64_t* cu_seqlens, int32_t num_seqs,
+                          int32_t H, int32_t D, int32_t block_size, int32_t topk, hipStream_t stream) {
+  Packed pk;
+  int64_t T = 0;
+  const int s = parse_packed(cu_seqlens, num_seqs, block_size, topk, &pk, &T);
+  if (s != MOBA_OK) return s;
+  return gate_impl(q, k, sel, T, H, D, block_size, topk, stream, false, Pooling(), &pk);
+}
+
+int moba_prefill_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                            const int64_t* cu_seqlens, int32_t num_seqs, int32_t H, int32_t D, int32_t block_size,
+                            int32_t topk, hipStream_t stream) {
+  Packed pk;
+  int64_t T = 0;
+  const int s = parse_packed(cu_seqlens, num_seqs, block_size, topk, &pk, &T);
+  if (s != MOBA_OK) return s;
+  return prefill_impl(q, k, v, out, lse, T, H, D, block_size, topk, stream, false, nullptr, Pooling(), &pk);
+}
+
+int moba_prefill_bwd_varlen(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                            const void* dout, void* dq, void* dk, void* dv, const int64_t* cu_seqlens,
+                            int32_t num_seqs, int32_t H, int32_t D, int32_t block_size, int32_t topk,
+                            hipStream_t stream) {
+  Packed pk;
+  int64_t T = 0;
+  const int s = parse_packed(cu_seqlens, num_seqs, block_size, topk, &pk, &T);
+  if (s != MOBA_OK) return s;
+  return backward_impl(q, k, v, out, lse, dout, dq, dk, dv, T, H, D, block_size, topk, stream, Pooling(), &pk);
 }
 
 int32_t moba_topk_for_sparsity(int64_t N, int32_t block_size, double sparsity) {

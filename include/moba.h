@@ -137,6 +137,30 @@ int moba_prefill_bwd_pooled(const void* q, const void* k, const void* v, const f
                             int32_t D, int32_t block_size, int32_t topk, int32_t pooling, hipStream_t stream);
 
 /*
+ * Packed (varlen) batches: num_seqs independent sequences concatenated along
+ * the token axis, the FlashAttention-style packing the pages build on (智东西
+ * report, section 二, implementation steps: varlen attention over reordered
+ * queries). cu_seqlens is a HOST array of num_seqs + 1 token offsets (0, then
+ * non-decreasing; T = cu_seqlens[num_seqs] tokens in all), read during the call;
+ * every sequence length must be a multiple of block_size (empty sequences are
+ * allowed). Blocks never straddle sequences, and a query's gate only sees the
+ * past blocks of its own sequence: each sequence gets exactly what a separate
+ * call on it would give. q, k, v, out, dout, dq, dk, dv: bf16 [T][H][D]; lse:
+ * fp32 [H][T]; sel: int32 [H][T][topk] with global block indices. At most 512
+ * sequences (MOBA_ERR_UNSUPPORTED above); a bad cu_seqlens is
+ * MOBA_ERR_INVALID_ARG. These calls never take the dense path.
+ */
+int moba_gate_topk_varlen(const void* q, const void* k, int32_t* sel, const int64_t* cu_seqlens, int32_t num_seqs,
+                          int32_t H, int32_t D, int32_t block_size, int32_t topk, hipStream_t stream);
+int moba_prefill_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                            const int64_t* cu_seqlens, int32_t num_seqs, int32_t H, int32_t D, int32_t block_size,
+                            int32_t topk, hipStream_t stream);
+int moba_prefill_bwd_varlen(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                            const void* dout, void* dq, void* dk, void* dv, const int64_t* cu_seqlens,
+                            int32_t num_seqs, int32_t H, int32_t D, int32_t block_size, int32_t topk,
+                            hipStream_t stream);
+
+/*
  * Dynamic k (host only, no GPU work): the top_k that keeps a late query's
  * sparsity 1 - block_size * k / N at `sparsity` for a context of N tokens,
  * k = nearest integer to (1 - sparsity) * N / block_size (ties to even),
@@ -149,7 +173,9 @@ int moba_prefill_bwd_pooled(const void* q, const void* k, const void* v, const f
 int32_t moba_topk_for_sparsity(int64_t N, int32_t block_size, double sparsity);
 
 /*
- * Full MoBA causal prefill: out[t][h][:] = softmax over the attended keys of
+ * Full MoBA causal prefill (when topk >= n every block is kept and the call
+ * runs as causal attention over the whole sequence: no gate, lists or
+ * partials): out[t][h][:] = softmax over the attended keys of
  * q_t . k_s / sqrt(D), applied to v, where the attended keys are every key of
  * the chosen past blocks and the keys of the own block up to t itself; lse as
  * in the conventions. Implements the five steps of the 智东西 report, section

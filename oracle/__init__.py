@@ -9,8 +9,10 @@ from .moba_oracle import (  # noqa: F401
     attended_pairs_closed_form,
     gate_scores,
     moba_backward_ref,
+    moba_backward_ref_varlen,
     moba_decode_ref,
     moba_ref,
+    moba_ref_varlen,
     n_blocks,
     pooled_keys,
     pooled_keys_fp32,

@@ -51,6 +51,10 @@ k, so no gradient flows through it or through the block means: the selection
 is held fixed and the gradients are those of the masked softmax attention over
 A(t) (the textbook softmax Jacobian).
 
+``moba_ref_varlen`` and ``moba_backward_ref_varlen`` take a packed batch of
+independent sequences (token offsets ``cu_seqlens``, each length a multiple of
+B) and apply the single-sequence definitions to each one.
+
 ``moba_decode_ref`` is the generation step after the prefill: the newest token
 (position N - 1 of a cache whose length need not be a multiple of B, so its
 own block may be partial) gated and attended exactly like a prefill row; with
@@ -521,3 +525,51 @@ def moba_backward_ref(q, k, v, dout, block_size: int, topk: int, sel=None, heads
     else:
         raise ValueError(method)
     return dq, dk, dv, sel
+
+
+def _segments(cu_seqlens, block_size: int):
+    cu = [int(x) for x in cu_seqlens]
+    if len(cu) < 2 or cu[0] != 0:
+        raise ValueError("cu_seqlens must start at 0 and hold num_seqs + 1 offsets")
+    segs = []
+    for a, b in zip(cu[:-1], cu[1:]):
+        if b < a or (b - a) % block_size != 0:
+            raise ValueError("sequence lengths must be non-negative multiples of block_size")
+        segs.append((a, b))
+    return segs
+
+
+def moba_ref_varlen(q, k, v, cu_seqlens, block_size: int, topk: int):
+    """Packed (varlen) batch: independent sequences concatenated along the token
+    axis, cu_seqlens their token offsets. Each sequence is its own MoBA prefill
+    (its blocks start at its first token; its queries see only its blocks):
+    out [T, H, D], lse [H, T] and sel [H, T, topk] with global block indices."""
+    q = np.asarray(q)
+    T, H, D = q.shape
+    out = np.zeros((T, H, D), np.float64)
+    lse = np.zeros((H, T), np.float64)
+    sel = np.full((H, T, topk), -1, np.int32)
+    for a, b in _segments(cu_seqlens, block_size):
+        if b == a:
+            continue
+        o, l, s = moba_ref(q[a:b], k[a:b], v[a:b], block_size, topk)
+        out[a:b] = o
+        lse[:, a:b] = l
+        sel[:, a:b] = np.where(s >= 0, s + a // block_size, -1)
+    return out, lse, sel
+
+
+def moba_backward_ref_varlen(q, k, v, dout, cu_seqlens, block_size: int, topk: int, sel=None):
+    """Gradients of ``moba_ref_varlen``: every sequence on its own. ``sel``
+    (global block indices, [H, T, topk]) optionally fixes the selection."""
+    q = np.asarray(q)
+    T, H, D = q.shape
+    grads = [np.zeros((T, H, D), np.float64) for _ in range(3)]
+    for a, b in _segments(cu_seqlens, block_size):
+        if b == a:
+            continue
+        s = None if sel is None else np.where(sel[:, a:b] >= 0, sel[:, a:b] - a // block_size, -1)
+        dq, dk, dv, _ = moba_backward_ref(q[a:b], k[a:b], v[a:b], dout[a:b], block_size, topk, sel=s)
+        for g, x in zip(grads, (dq, dk, dv)):
+            g[a:b] = x
+    return tuple(grads)

@@ -602,6 +602,52 @@ def pin_topk_for_sparsity(m):
     assert ks == sorted(ks) and ks[0] == 1 and ks[-1] == round(0.047 * 2048)
 
 
+# ---------------------------------------------------------------------------
+# packed (varlen) batches
+# ---------------------------------------------------------------------------
+
+def pin_varlen_brute(m):
+    """Packed batch on tiny inputs: masked SDPA over the whole packed axis with a
+    mask that is block-diagonal by sequence, from per-sequence exhaustive
+    selections; gradients through autograd of the same masked SDPA."""
+    B, topk, H, D = 4, 3, 2, 4
+    cu = [0, 16, 16, 40, 48]
+    T = cu[-1]
+    q, k, v = _rand(T, H, D, 81)
+    do = np.random.default_rng(82).standard_normal((T, H, D))
+    out, lse, sel = m.moba_ref_varlen(q, k, v, cu, B, topk)
+    dq, dk, dv = m.moba_backward_ref_varlen(q, k, v, do, cu, B, topk)
+    for h in range(H):
+        mask = torch.zeros((T, T), dtype=torch.bool)
+        for a, b in zip(cu[:-1], cu[1:]):
+            if b == a:
+                continue
+            bs = brute_selection(q[a:b], k[a:b], B, topk)
+            assert np.array_equal(np.where(bs[h] >= 0, bs[h] + a // B, -1), sel[h, a:b])
+            mask[a:b, a:b] = _brute_mask(bs[h], b - a, B)
+        qh, kh, vh = (_t64(x[:, h]) for x in (q, k, v))
+        ref = torch.nn.functional.scaled_dot_product_attention(qh[None], kh[None], vh[None], attn_mask=mask[None])[0]
+        assert np.allclose(out[:, h], ref.numpy(), atol=1e-12, rtol=0)
+        rl = torch.logsumexp(((qh @ kh.T) / math.sqrt(D)).masked_fill(~mask, -math.inf), -1)
+        assert np.allclose(lse[h], rl.numpy(), atol=1e-12, rtol=0)
+        rq, rk, rv = _autograd_masked(q[:, h], k[:, h], v[:, h], do[:, h], mask)
+        for got, r in ((dq, rq), (dk, rk), (dv, rv)):
+            assert np.allclose(got[:, h], r, atol=1e-12, rtol=0)
+
+
+def pin_varlen_one_sequence_and_order(m):
+    """One sequence is the plain prefill; swapping two sequences swaps their outputs."""
+    B, topk = 8, 3
+    q, k, v = _rand(64, 2, 8, 83)
+    o1, l1, s1 = m.moba_ref(q, k, v, B, topk)
+    o2, l2, s2 = m.moba_ref_varlen(q, k, v, [0, 64], B, topk)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2) and np.array_equal(s1, s2)
+    perm = np.r_[np.arange(40, 64), np.arange(0, 40)]
+    oa, la, _ = m.moba_ref_varlen(q, k, v, [0, 40, 64], B, topk)
+    ob, lb, _ = m.moba_ref_varlen(q[perm], k[perm], v[perm], [0, 24, 64], B, topk)
+    assert np.allclose(oa[perm], ob, atol=1e-12, rtol=0) and np.allclose(la[:, perm], lb, atol=1e-12, rtol=0)
+
+
 ALL_PINS = [
     pin_bruteforce_tiny, pin_full_causal, pin_block_diagonal, pin_first_token, pin_constant_v,
     pin_zero_query, pin_invariants, pin_pages_worked_example, pin_pages_sparsity_table,
@@ -610,5 +656,5 @@ ALL_PINS = [
     pin_decode_first_token, pin_decode_brute_selection, pin_decode_matches_prefill_row,
     pin_backward_full_causal, pin_backward_block_diagonal, pin_backward_brute, pin_backward_finite_difference,
     pin_backward_invariants, pin_backward_methods_agree, pin_pooling_max, pin_pooling_weighted,
-    pin_topk_for_sparsity,
+    pin_topk_for_sparsity, pin_varlen_brute, pin_varlen_one_sequence_and_order,
 ]

@@ -200,3 +200,23 @@ def test_pooled_argument_checks(lib):
     assert lib.moba_block_pool_keys(A, None, A, 1024, 2, 128, 128, -1, None) == INVALID
     assert lib.moba_prefill_fwd_pooled(A, A, A, None, A, A, 1024, 2, 128, 128, 3, 2, None) == INVALID
     assert lib.moba_prefill_bwd_pooled(A, A, A, None, A, A, A, A, A, A, 1024, 2, 128, 128, 3, 7, None) == INVALID
+
+
+def test_varlen_argument_checks(lib):
+    def cu(*xs):
+        arr = (ctypes.c_int64 * len(xs))(*xs)
+        return arr
+
+    g = lib.moba_prefill_fwd_varlen
+    ok = cu(0, 256, 512)
+    assert g(A, A, A, A, A, None, 2, 2, 128, 128, 3, None) == INVALID            # no cu_seqlens
+    assert g(A, A, A, A, A, ok, 0, 2, 128, 128, 3, None) == INVALID              # no sequences
+    assert g(A, A, A, A, A, cu(1, 257, 513), 2, 2, 128, 128, 3, None) == INVALID  # not starting at 0
+    assert g(A, A, A, A, A, cu(0, 300, 512), 2, 2, 128, 128, 3, None) == INVALID  # length not a multiple of B
+    assert g(A, A, A, A, A, cu(0, 512, 256), 2, 2, 128, 128, 3, None) == INVALID  # decreasing offsets
+    assert g(A, A, A, A, A, cu(0, 0, 0), 2, 2, 128, 128, 3, None) == INVALID      # no tokens
+    assert g(A, A, A, A, A, ok, 513, 2, 128, 128, 3, None) == UNSUPPORTED         # too many sequences
+    assert g(A, A, A, A, A, cu(0, 128 * 40, 128 * 41), 2, 2, 128, 128, 33, None) == UNSUPPORTED
+    assert g(None, A, A, A, A, ok, 2, 2, 128, 128, 3, None) == INVALID
+    assert lib.moba_gate_topk_varlen(A, A, A, cu(0, 300), 1, 2, 128, 128, 3, None) == INVALID
+    assert lib.moba_prefill_bwd_varlen(A, A, A, A, A, A, A, A, A, ok, 2, 2, 96, 128, 3, None) == UNSUPPORTED

@@ -68,6 +68,13 @@ MUTATIONS = {
     "weighted_weights_of_wrong_head": ("wb = w64.reshape(H, n, block_size).transpose(1, 2, 0)",
                                        "wb = w64[::-1].reshape(H, n, block_size).transpose(1, 2, 0)"),
     "dynamic_k_rounds_up": ("round((1.0 - sparsity) * N / block_size)", "math.ceil((1.0 - sparsity) * N / block_size)"),
+    "varlen_local_block_indices": ("sel[:, a:b] = np.where(s >= 0, s + a // block_size, -1)",
+                                   "sel[:, a:b] = s"),
+    "varlen_sequences_share_context": ("o, l, s = moba_ref(q[a:b], k[a:b], v[a:b], block_size, topk)",
+                                       "o, l, s = moba_ref(q[:b], k[:b], v[:b], block_size, topk); "
+                                       "o, l, s = o[a:], l[:, a:], s[:, a:]"),
+    "varlen_backward_wrong_segment": ("dq, dk, dv, _ = moba_backward_ref(q[a:b], k[a:b], v[a:b], dout[a:b], block_size, topk, sel=s)",
+                                      "dq, dk, dv, _ = moba_backward_ref(q[a:b], k[a:b], v[a:b], dout[::-1][a:b], block_size, topk, sel=s)"),
     "backward_scale_1_over_d": ("softmax_scale = 1.0 / math.sqrt(D)", "softmax_scale = 1.0 / D"),
     "backward_drops_row_sum": ("dl = p * (dp - np.sum(p * dp, axis=1, keepdims=True))", "dl = p * dp"),
     "backward_dk_unscaled": ("dk[:nk, oh] += scale * (dl.T @ qh)", "dk[:nk, oh] += dl.T @ qh"),
