@@ -244,10 +244,20 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
     }
     const char* qt = tiles[buf];
     const char* dt = tiles[buf] + L::kTile;
-    if (active) {
+    const bool own = i >= t_past;
+    const int q0 = own0 + kBwdQTile * (i - t_past);   // own tiles: offset of the tile's first query
+    if (active && own && kofs > q0 + 32 * wh + 31) {
+      // Every key of the group comes after every query of the half: P = dS = 0.
+      const bf16x4 z4 = {static_cast<bf16>(0.f), static_cast<bf16>(0.f), static_cast<bf16>(0.f),
+                         static_cast<bf16>(0.f)};
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int rq = wh * 32 + 8 * g4 + 4 * half;
+        *reinterpret_cast<bf16x4*>(xp + 2 * rq) = z4;
+        *reinterpret_cast<bf16x4*>(xp + 4 * kX + 2 * rq) = z4;
+      }
+    } else if (active) {
       // S and dP for key group kg and queries 32 wh .. 32 wh + 31 of the tile.
-      const bool own = i >= t_past;
-      const int q0 = own0 + kBwdQTile * (i - t_past);   // own tiles: offset of the tile's first query
       const f32x16 s = rows_by_regs<D>(qt + wh * 32 * L::kRow + row_lane, kr);
       const f32x16 dp = rows_by_regs<D>(dt + wh * 32 * L::kRow + row_lane, vr);
 #pragma unroll
@@ -271,7 +281,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
       }
     }
     __syncthreads();
-    if (active) {
+    if (active && !(own && kofs > q0 + kBwdQTile - 1)) {   // (all P = 0 otherwise)
       // dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS for dims kDH wh .. and the whole tile.
 #pragma unroll
       for (int g = 0; g < kBwdQTile / 16; ++g) {
@@ -393,6 +403,9 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
   const int tg = lane >> 4, te = (lane >> 2) & 3, tq = lane & 3;
   const int row_lane = col * L::kRow + 16 * half;
   const int tr_lane = (4 * (tg >> 1) + te) * L::kRow + 2 * (16 * (tg & 1) + 4 * tq);
+  // This wave's last query (wave-uniform): key halves after it are all masked
+  // (own items), and a wave without queries has nothing to add.
+  const int64_t wlast = 32 * w < count ? (kOwn ? t0 + min(32 * w + 31, count - 1) : INT64_MAX) : -1;
   fetch(0);
   commit(0);
   __syncthreads();
@@ -403,10 +416,11 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
     const char* vt = tiles[buf] + L::kTile;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
+      const int64_t kbase = kb0 + kBwdKTile * i + 32 * kh;
+      if (kbase > wlast) continue;
       const f32x16 s = rows_by_regs<D>(kt + kh * 32 * L::kRow + row_lane, qr);
       const f32x16 dp = rows_by_regs<D>(vt + kh * 32 * L::kRow + row_lane, dr);
       f32x16 ds;
-      const int64_t kbase = kb0 + kBwdKTile * i + 32 * kh;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float pr = __builtin_amdgcn_exp2f(fmaf(s[r], a.scale_log2, -lse2));

@@ -1,4 +1,7 @@
-"""CPU check of the compiled MFMA kernels: no private (scratch) memory.
+"""CPU check of the compiled kernels: no private (scratch) memory.
+
+(The backward and decode kernels keep their accumulators and operands in
+registers; a spill there would not change results either, only speed.)
 
 The attention and gate kernels count their own outstanding vector-memory
 operations and wait on exact counts. A register spilled to scratch and
@@ -40,7 +43,8 @@ def kernel_metadata(src, tmp_path):
     return meta
 
 
-@pytest.mark.parametrize("src,pattern", [("attn.hip", "attn_mfma_kernel"), ("gate.hip", "gate_mfma_kernel")])
+@pytest.mark.parametrize("src,pattern", [("attn.hip", "attn_mfma_kernel"), ("gate.hip", "gate_mfma_kernel"),
+                                         ("bwd.hip", "bwd_"), ("decode.hip", "decode_")])
 def test_mfma_kernels_use_no_scratch(src, pattern, tmp_path):
     meta = kernel_metadata(os.path.join(CSRC, src), tmp_path)
     kernels = {k: v for k, v in meta.items() if pattern in k}
