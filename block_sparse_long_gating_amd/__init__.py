@@ -70,6 +70,12 @@ def load_library():
     """Load libmoba.so (raises if it has not been built)."""
     global _lib
     if _lib is None:
+        # torch ships its own HIP runtime; importing it first makes the library
+        # bind to that one instead of loading a second runtime into the process.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         if not os.path.exists(_LIB_PATH):
             raise RuntimeError(f"{_LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
         lib = ctypes.CDLL(_LIB_PATH)
