@@ -542,6 +542,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
   // ---- static schedule of this workgroup ----
   int64_t first, stride;
   int cnt;
+  int gper = 0, gside = 0;   // grouped own-block schedule: group size and this workgroup's place in it
   if (!kCausal) {
     const int64_t M = a.counters[0];
     const int xcd = blockIdx.x % kXcds, c = blockIdx.x / kXcds, nper = gridDim.x / kXcds;
@@ -550,13 +551,35 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
     stride = nper;
     cnt = first < xb ? static_cast<int>((xb - first + nper - 1) / nper) : 0;
   } else {
-    const int64_t lo = a.own_items * blockIdx.x / gridDim.x, hi = a.own_items * (blockIdx.x + 1) / gridDim.x;
-    first = lo;
-    stride = 1;
-    cnt = static_cast<int>(hi - lo);
+    const int per = a.qt_per_block;
+    const int64_t nblk = a.own_items / per;
+    const int G = static_cast<int>(gridDim.x);
+    if (per > 1 && G % (kXcds * per) == 0) {
+      // The per query tiles of a block run at the same time on `per`
+      // workgroups of one XCD, which then read the block's K/V tiles once from
+      // HBM and share them in L2; the tiles rotate over the group's workgroups
+      // from one block to the next, which evens out the causal work.
+      const int x = static_cast<int>(blockIdx.x) % kXcds, sx = static_cast<int>(blockIdx.x) / kXcds;
+      const int64_t groups = G / per;
+      first = static_cast<int64_t>(x) * (G / kXcds / per) + sx / per;   // this group's first block
+      stride = groups;
+      gper = per;
+      gside = sx % per;
+      cnt = first < nblk ? static_cast<int>((nblk - first + groups - 1) / groups) : 0;
+    } else {
+      const int64_t lo = a.own_items * blockIdx.x / gridDim.x, hi = a.own_items * (blockIdx.x + 1) / gridDim.x;
+      first = lo;
+      stride = 1;
+      cnt = static_cast<int>(hi - lo);
+    }
   }
   cnt = static_cast<int>(uniform_u32(cnt));
   if (cnt <= 0) return;
+  // The m-th item of this workgroup.
+  auto sched = [&](int m) -> int64_t {
+    const int64_t base = first + static_cast<int64_t>(m) * stride;
+    return (kCausal && gper > 0) ? base * gper + (gside + m) % gper : base;
+  };
 
   // ---- per-lane offsets of the K/V tile loads (tile-relative) ----
   uint32_t kvoff[L::kRoundsHi];
@@ -661,7 +684,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
   };
 
   // ---- prologue ----
-  Desc dd = item_desc<kCausal, kFused>(a, first);     // item being loaded
+  Desc dd = item_desc<kCausal, kFused>(a, sched(0));   // item being loaded
   int md = 0, jd = 0;                         // load cursor: item ordinal, step within item
   bool ddone = false;
   int qstep0 = -1000, qstep1 = -1000;         // ring step at which each qbuf was requested
@@ -676,7 +699,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
       if (md + 1 < cnt) {
         ++md;
         jd = 0;
-        dd = item_desc<kCausal, kFused>(a, first + static_cast<int64_t>(md) * stride);
+        dd = item_desc<kCausal, kFused>(a, sched(md));
       } else {
         ddone = true;   // keep re-loading the last K/V tile (into slots nobody reads again)
         jd = 2 + dd.nkt - 1;
@@ -810,14 +833,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
       for (int e = 0; e < 8; ++e) va1[dc][g][e] = static_cast<bf16>(0.f);
 
   for (int mc = 0; mc < cnt; ++mc) {
-    const Desc cd = item_desc<kCausal, kFused>(a, first + static_cast<int64_t>(mc) * stride);
+    const Desc cd = item_desc<kCausal, kFused>(a, sched(mc));
     bf16x8 q[kQC];
     {
       // The first Q step also requests the query indices of the next item
       // (past-block items) or this item's list positions (fused merge).
       const bool more = mc + 1 < cnt;
       Desc nd = cd;
-      if (!kCausal && more) nd = item_desc<kCausal, kFused>(a, first + static_cast<int64_t>(mc + 1) * stride);
+      if (!kCausal && more) nd = item_desc<kCausal, kFused>(a, sched(mc + 1));
       const char* slot = ring_step(kFused ? 0 : (!kCausal && more ? (mc + 1) & 1 : -1), nd, false);
       if (w < 4) {
 #pragma unroll
