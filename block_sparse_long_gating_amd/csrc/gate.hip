@@ -331,9 +331,10 @@ hipError_t launch_gate_t(const Problem& p, const void* q, const Workspace& ws, i
     gate_f32_kernel<D, KCAP><<<grid, 256, smem, stream>>>(static_cast<const float*>(q), ws.kbar, a);
     return hipGetLastError();
   }
-  // Persistent: a few workgroups per CU over all heads, each walking every
+  // Persistent: three workgroups per CU (as many as the staged means of a
+  // 64-block head leave room for in LDS) over all heads, each walking every
   // grid.x-th tile of its head.
-  const int per_head = std::max(1, std::min(p.ntiles, (6 * num_cus + p.H - 1) / p.H));
+  const int per_head = std::max(1, std::min(p.ntiles, (3 * num_cus + p.H - 1) / p.H));
   dim3 grid(per_head, p.H);
   const size_t lds_pieces = static_cast<size_t>(p.n) * gate_lds_row<D>();
   const size_t bm1 = static_cast<size_t>(4) * p.n * sizeof(uint32_t);
