@@ -300,7 +300,187 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   }
 }
 
+// Gated decode in one launch: one 1024-thread workgroup per head gates, attends
+// its kept keys and combines them in LDS (no workspace). For a few thousand
+// kept keys, where three launches and a workspace cost more than the work.
+constexpr int kFusedThreads = 1024;
+constexpr int kFusedKeys = 8;          // keys in flight per lane group
+
+template <int D>
+__global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(DecodeArgs a) {
+  constexpr int kL = D / 8;                          // lanes per row (8 dims each)
+  constexpr int kGroups = kFusedThreads / kL;        // lane groups
+  constexpr int kWavesF = kFusedThreads / 64;
+  __shared__ float sc[kDecLdsScores];
+  __shared__ uint64_t red[kWavesF];
+  __shared__ int chosen[kDecMaxPast];
+  __shared__ int srow[kDecMaxPast + 1];
+  __shared__ float sm_m[kGroups], sm_l[kGroups];
+  __shared__ float sm_o[kGroups][D];
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = tid % kL, g = tid / kL;
+  const int j = a.j, S = a.S;                        // j >= topk here: the gate chooses
+  // ---- gate: fp32 scores of the complete past blocks, then k - 1 arg-max rounds ----
+  float qf[8];
+  {
+    const bf16x8 q8 = load_bf16x8(a.q + static_cast<int64_t>(h) * D + 8 * li);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[e] = static_cast<float>(q8[e]);
+  }
+  const float* kb = a.kbar + static_cast<int64_t>(h) * a.kbar_blocks * D + 8 * li;
+  for (int i0 = g; i0 < j; i0 += 4 * kGroups) {
+    float4 x[4][2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = min(i0 + u * kGroups, j - 1);
+      const float4* p = reinterpret_cast<const float4*>(kb + static_cast<int64_t>(i) * D);
+      x[u][0] = p[0];
+      x[u][1] = p[1];
+    }
+    float sv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sv[u] = dot8(qf, x[u][0], x[u][1]);
+#pragma unroll
+    for (int w = 1; w < kL; w <<= 1)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sv[u] += __shfl_xor(sv[u], w);
+    if (li == 0)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (i0 + u * kGroups < j) sc[i0 + u * kGroups] = sv[u];
+  }
+  __syncthreads();
+  const int nk = a.topk - 1;
+  for (int r = 0; r < nk; ++r) {
+    uint64_t best = 0;
+    for (int i = tid; i < j; i += kFusedThreads) {
+      bool taken = false;
+      for (int c = 0; c < r; ++c) taken |= chosen[c] == i;
+      if (!taken) {
+        const uint64_t key = rank_key(sc[i], i);
+        best = key > best ? key : best;
+      }
+    }
+#pragma unroll
+    for (int w = 32; w >= 1; w >>= 1) {
+      const uint64_t o = __shfl_xor(best, w);
+      best = o > best ? o : best;
+    }
+    if (lane == 0) red[wave] = best;
+    __syncthreads();
+    if (tid == 0) {
+      uint64_t m = red[0];
+      for (int x = 1; x < kWavesF; ++x) m = red[x] > m ? red[x] : m;
+      chosen[r] = key_block(m);
+    }
+    __syncthreads();
+  }
+  if (tid < nk) {
+    const int b = chosen[tid];
+    int pos = 0;
+    for (int c = 0; c < nk; ++c) pos += chosen[c] < b ? 1 : 0;
+    srow[pos] = b;
+  }
+  if (tid == 0) srow[nk] = j;
+  __syncthreads();
+  if (a.sel_out != nullptr && tid < a.topk)
+    a.sel_out[static_cast<int64_t>(h) * a.topk + tid] = tid < S ? srow[tid] : -1;
+  // ---- attention over the kept keys: (S - 1) full blocks, then the own block up to t ----
+  const int64_t t = a.N - 1;
+  const int nkeys = (S - 1) * a.B + static_cast<int>(t - static_cast<int64_t>(j) * a.B) + 1;
+  const int64_t row_el = static_cast<int64_t>(a.H) * D;
+  const int64_t col = static_cast<int64_t>(h) * D + 8 * li;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) qf[e] *= a.scale_log2;
+  float m = -INFINITY, l = 0.f, o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
+  // This lane group's kept key f = g, g + kGroups, ... as (slot, offset in the
+  // block), advanced incrementally (no division per key).
+  int slot = g / a.B, off = g % a.B;
+  int64_t last_key = t;                                 // the final kept key (the token itself)
+  for (int f0 = g; f0 < nkeys; f0 += kFusedKeys * kGroups) {
+    bf16x8 k8[kFusedKeys], v8[kFusedKeys];
+#pragma unroll
+    for (int x = 0; x < kFusedKeys; ++x) {
+      // Past the end: re-read the last key (masked below).
+      const int64_t key = f0 + x * kGroups < nkeys ? static_cast<int64_t>(srow[slot]) * a.B + off : last_key;
+      k8[x] = load_bf16x8(a.k + key * row_el + col);
+      v8[x] = load_bf16x8(a.v + key * row_el + col);
+      off += kGroups;
+      while (off >= a.B && slot < S - 1) {
+        off -= a.B;
+        ++slot;
+      }
+    }
+    float sv[kFusedKeys];
+#pragma unroll
+    for (int x = 0; x < kFusedKeys; ++x) {
+      sv[x] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sv[x] = fmaf(qf[e], static_cast<float>(k8[x][e]), sv[x]);
+    }
+#pragma unroll
+    for (int w = 1; w < kL; w <<= 1)
+#pragma unroll
+      for (int x = 0; x < kFusedKeys; ++x) sv[x] += __shfl_xor(sv[x], w);
+    float mn = m;
+#pragma unroll
+    for (int x = 0; x < kFusedKeys; ++x) {
+      if (f0 + x * kGroups >= nkeys) sv[x] = -INFINITY;
+      mn = fmaxf(mn, sv[x]);
+    }
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    float ps = 0.f, pr[kFusedKeys];
+#pragma unroll
+    for (int x = 0; x < kFusedKeys; ++x) {
+      pr[x] = __builtin_amdgcn_exp2f(sv[x] - mn);
+      ps += pr[x];
+    }
+    l = fmaf(l, alpha, ps);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float pv = 0.f;
+#pragma unroll
+      for (int x = 0; x < kFusedKeys; ++x) pv = fmaf(pr[x], static_cast<float>(v8[x][e]), pv);
+      o[e] = fmaf(o[e], alpha, pv);
+    }
+    m = mn;
+  }
+  if (li == 0) {
+    sm_m[g] = m;
+    sm_l[g] = l;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sm_o[g][8 * li + e] = o[e];
+  __syncthreads();
+  if (tid < D) {
+    float mt = -INFINITY;
+    for (int x = 0; x < kGroups; ++x) mt = fmaxf(mt, sm_m[x]);
+    float od = 0.f, lt = 0.f;
+    for (int x = 0; x < kGroups; ++x) {
+      const float w = sm_m[x] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm_m[x] - mt);
+      od = fmaf(sm_o[x][tid], w, od);
+      lt = fmaf(sm_l[x], w, lt);
+    }
+    a.out[static_cast<int64_t>(h) * D + tid] = static_cast<bf16>(od / lt);
+    if (tid == 0) a.lse[h] = (mt + log2f(lt)) * kDecLn2;
+  }
+}
+
 }  // namespace
+
+bool decode_fused(const DecodeArgs& a) {
+  const int64_t keys = static_cast<int64_t>(a.S - 1) * a.B + (a.N - 1 - static_cast<int64_t>(a.j) * a.B) + 1;
+  return a.kbar != nullptr && a.S < a.j + 1 && a.j <= kDecLdsScores && keys <= kDecFusedMaxKeys;
+}
+
+hipError_t launch_decode_fused(const DecodeArgs& a, hipStream_t stream) {
+  if (a.D == 128) decode_fused_kernel<128><<<a.H, kFusedThreads, 0, stream>>>(a);
+  else decode_fused_kernel<64><<<a.H, kFusedThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid(a.units, a.H);

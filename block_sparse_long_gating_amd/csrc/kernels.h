@@ -89,6 +89,11 @@ struct DecodeArgs {
   float scale_log2;     // log2(e) / sqrt(D)
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// One-launch gated decode (no workspace): the caller's block means, a gate
+// choice to make, at most 2048 past blocks and kDecFusedMaxKeys kept keys.
+constexpr int kDecFusedMaxKeys = 8192;
+bool decode_fused(const DecodeArgs& a);
+hipError_t launch_decode_fused(const DecodeArgs& a, hipStream_t stream);
 
 // Backward pass of the bf16 prefill: dQ, dK, dV of the output (the selection
 // and the query lists come from the gate and list stages of the same call).

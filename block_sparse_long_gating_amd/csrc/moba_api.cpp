@@ -457,6 +457,19 @@ int decode_impl(const void* q, const void* k, const void* v, const float* kbar, 
   if (static_cast<int64_t>(a.S) * a.chunks >= (int64_t{1} << 31)) return MOBA_ERR_UNSUPPORTED;
   a.units = a.S * a.chunks;
   a.scale_log2 = 1.4426950408889634f / std::sqrt(static_cast<float>(D));
+  a.q = static_cast<const moba::bf16*>(q);
+  a.k = static_cast<const moba::bf16*>(k);
+  a.v = static_cast<const moba::bf16*>(v);
+  a.kbar = kbar;
+  a.kbar_blocks = kbar_blocks;
+  a.sel_out = sel;
+  a.out = static_cast<moba::bf16*>(out);
+  a.lse = lse;
+  if (moba::decode_fused(a)) {
+    // Caller's block means and few kept keys: one launch, no workspace.
+    const hipError_t e = moba::launch_decode_fused(a, stream);
+    return e == hipSuccess ? MOBA_OK : hip_fail(e);
+  }
   const bool own_kbar = kbar == nullptr && topk < j + 1;   // block means only matter when the gate chooses
   Layout L;
   const size_t o_sel = L.add(static_cast<size_t>(H) * a.S * 4);

@@ -225,6 +225,7 @@ DECODE = [
     (3333, 2, 128, 1000, 2, 8),
     (32768, 8, 128, 512, 3, 9),
     (140000, 1, 64, 64, 4, 10),      # 2187 past blocks: gate scores outside LDS
+    (32768, 2, 128, 512, 16, 11),    # 8192 kept keys: the largest one-launch step
 ]
 
 
@@ -244,12 +245,14 @@ def test_decode_parity(moba, case):
         # Exact fp64 means rounded once to fp32, as moba_block_mean_keys writes them
         # (computed here with torch so that any block size works).
         kbar = kd[:j * B].double().reshape(j, B, H, D).mean(dim=1).float().permute(1, 0, 2).contiguous()
-        out2, lse2 = moba.decode(qn, kd, vd, B, topk, kbar=kbar)
     else:
-        out2, lse2 = moba.decode(qn, kd, vd, B, topk)
+        kbar = None
+    # With the means supplied, a gated step with few kept keys runs as one
+    # launch (a different summation order): same selection, outputs to the bar.
+    sel2 = torch.empty_like(sel)
+    out2, lse2 = moba.decode(qn, kd, vd, B, topk, kbar=kbar, sel=sel2)
     torch.cuda.synchronize()
-    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
-    assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
+    assert torch.equal(sel, sel2)
     gsel = sel.cpu().numpy()
     _, _, rsel = moba_decode_ref(q[N - 1], k, v, B, topk)
     exempt = 0
@@ -264,8 +267,8 @@ def test_decode_parity(moba, case):
         assert len(a) == len(b) and np.all(np.abs(np.array(a) - np.array(b)) <= TIE_REL * np.max(np.abs(g[:j])))
         exempt += 1
     ro, rl, _ = moba_decode_ref(q[N - 1], k, v, B, topk, sel=gsel)
-    err_o = max_abs(out.float().cpu().numpy(), ro)
-    err_l = max_abs(lse.cpu().numpy(), rl)
+    err_o = max(max_abs(out.float().cpu().numpy(), ro), max_abs(out2.float().cpu().numpy(), ro))
+    err_l = max(max_abs(lse.cpu().numpy(), rl), max_abs(lse2.cpu().numpy(), rl))
     log(f"  decode N={N} H={H} D={D} B={B} k={topk}: exempt {exempt}, max|out| err {err_o:.3e}, max|lse| err {err_l:.3e}")
     assert err_o <= OUT_TOL["bf16"]
     assert err_l <= LSE_TOL["bf16"]
