@@ -6,7 +6,7 @@
 // that kept that block, ordered by query position:
 //   1. scan_tiles: per (head, block), exclusive prefix of the per-tile counts
 //      written by the gate, and the list length;
-//   2. build_lists (one workgroup): global start of every list and the work
+//   2. build_lists (one 1024-thread workgroup): global start of every list and the work
 //      items of at most kAttnTile list entries each;
 //   3. scatter: every (query, kept past block) pair lands at
 //      start(list) + prefix(tile) + rank-in-tile; the position is also kept per
@@ -19,26 +19,39 @@ namespace moba {
 
 namespace {
 
-// Workgroup-wide exclusive scan of one int64 value per thread (256 threads).
+// Workgroup-wide exclusive scan of one int64 value per thread (NT threads, a
+// multiple of 64): shuffle scans inside each wave, then a scan of the wave totals.
+template <int NT>
 __device__ __forceinline__ int64_t block_exclusive_scan(int64_t x, int64_t* sh, int64_t* total) {
-  const int tid = threadIdx.x;
-  sh[tid] = x;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int64_t y = tid >= off ? sh[tid - off] : 0;
-    __syncthreads();
-    sh[tid] += y;
-    __syncthreads();
+  constexpr int kW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int64_t v = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t y = __shfl_up(v, off);
+    if (lane >= off) v += y;
   }
-  const int64_t incl = sh[tid];
-  *total = sh[255];
+  if (lane == 63) sh[wave] = v;
   __syncthreads();
-  return incl - x;
+  if (wave == 0) {
+    int64_t wv = lane < kW ? sh[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < kW; off <<= 1) {
+      const int64_t y = __shfl_up(wv, off);
+      if (lane >= off) wv += y;
+    }
+    if (lane < kW) sh[lane] = wv;
+  }
+  __syncthreads();
+  const int64_t base = wave > 0 ? sh[wave - 1] : 0;
+  *total = sh[kW - 1];
+  __syncthreads();
+  return base + v - x;
 }
 
 __global__ __launch_bounds__(256) void scan_tiles_kernel(int32_t* __restrict__ cnt, int32_t* __restrict__ totals,
                                                          int ntiles) {
-  __shared__ int64_t sh[256];
+  __shared__ int64_t sh[4];
   const int64_t e = blockIdx.x;
   int32_t* row = cnt + e * ntiles;
   const int per = (ntiles + 255) / 256;
@@ -47,7 +60,7 @@ __global__ __launch_bounds__(256) void scan_tiles_kernel(int32_t* __restrict__ c
   int64_t s = 0;
   for (int i = lo; i < hi; ++i) s += row[i];
   int64_t total;
-  int64_t run = block_exclusive_scan(s, sh, &total);
+  int64_t run = block_exclusive_scan<256>(s, sh, &total);
   for (int i = lo; i < hi; ++i) {
     const int32_t c = row[i];
     row[i] = static_cast<int32_t>(run);
@@ -56,11 +69,14 @@ __global__ __launch_bounds__(256) void scan_tiles_kernel(int32_t* __restrict__ c
   if (threadIdx.x == 0) totals[e] = static_cast<int32_t>(total);
 }
 
-__global__ __launch_bounds__(256) void build_lists_kernel(const int32_t* __restrict__ totals,
-                                                          int32_t* __restrict__ offs, WorkItem* __restrict__ items,
-                                                          int32_t* __restrict__ counters, int n, int64_t E) {
-  __shared__ int64_t sh[256];
-  const int64_t per = (E + 255) / 256;
+constexpr int kListThreads = 1024;
+
+__global__ __launch_bounds__(kListThreads) void build_lists_kernel(const int32_t* __restrict__ totals,
+                                                                   int32_t* __restrict__ offs,
+                                                                   WorkItem* __restrict__ items,
+                                                                   int32_t* __restrict__ counters, int n, int64_t E) {
+  __shared__ int64_t sh[kListThreads / 64];
+  const int64_t per = (E + kListThreads - 1) / kListThreads;
   const int64_t lo = min(E, static_cast<int64_t>(threadIdx.x) * per);
   const int64_t hi = min(E, lo + per);
   int64_t s_len = 0, s_items = 0;
@@ -70,8 +86,8 @@ __global__ __launch_bounds__(256) void build_lists_kernel(const int32_t* __restr
     s_items += (len + kAttnTile - 1) / kAttnTile;
   }
   int64_t tot_len, tot_items;
-  int64_t pos = block_exclusive_scan(s_len, sh, &tot_len);
-  int64_t it = block_exclusive_scan(s_items, sh, &tot_items);
+  int64_t pos = block_exclusive_scan<kListThreads>(s_len, sh, &tot_len);
+  int64_t it = block_exclusive_scan<kListThreads>(s_items, sh, &tot_items);
   for (int64_t e = lo; e < hi; ++e) {
     const int64_t len = totals[e];
     offs[e] = static_cast<int32_t>(pos);
@@ -118,7 +134,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
 hipError_t launch_csr(const Problem& p, const Workspace& ws, const int32_t* sel, hipStream_t stream) {
   const int64_t E = static_cast<int64_t>(p.H) * p.n;
   scan_tiles_kernel<<<static_cast<unsigned>(E), 256, 0, stream>>>(ws.cnt, ws.totals, p.ntiles);
-  build_lists_kernel<<<1, 256, 0, stream>>>(ws.totals, ws.offs, ws.items, ws.counters, p.n, E);
+  build_lists_kernel<<<1, kListThreads, 0, stream>>>(ws.totals, ws.offs, ws.items, ws.counters, p.n, E);
   const int64_t threads = p.N * p.H;
   if (p.lmax > 0)
     scatter_kernel<<<static_cast<unsigned>((threads + 255) / 256), 256, 0, stream>>>(
