@@ -43,6 +43,7 @@ SMALL = [
     (1024, 2, 128, 128, 4, "fp32", 12),
     (640, 1, 64, 64, 5, "fp32", 13),
     (4096, 1, 128, 64, 32, "bf16", 14),
+    (1024, 40, 64, 128, 4, "bf16", 15),      # many heads, not a power of two
 ]
 
 
@@ -488,3 +489,27 @@ def test_varlen_parity(moba, case):
         torch.cuda.synchronize()
         err = float((o1.float() - out[a:b].float()).abs().max())
         assert err <= 2 * OUT_TOL["bf16"], (a, b, err)
+
+
+def test_largest_block_count(moba):
+    """n = 4096 blocks (the largest supported) with top-32 (the widest ranked
+    list): the gate reads the split means from L2 and keeps one bitmap buffer,
+    every query keeps 31 past blocks (the separate merge). Sampled rows."""
+    from oracle import moba_ref, select_blocks
+    N, H, D, B, topk = 262144, 1, 64, 64, 32
+    q, k, v = synth.make_qkv(N, H, D, seed=[540, 0], dtype="bf16")
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    sel = moba.gate_topk(qd, kd, B, topk)
+    out, lse = moba.prefill(qd, kd, vd, B, topk)
+    torch.cuda.synchronize()
+    rows = synth.sample_rows(N, 1024, 541)
+    gsel = sel.cpu().numpy()[:, rows]
+    ref_sel, _ = select_blocks(q, k, B, topk, rows=rows)
+    cmp = compare_selection(gsel, ref_sel, q, k, B, topk, rows=rows)
+    assert not cmp["bad"], cmp["bad"][:3]
+    ref_out, ref_lse, _ = moba_ref(q, k, v, B, topk, sel=gsel, rows=rows, method="blocks")
+    e_out = max_abs(out.float().cpu().numpy()[rows], ref_out)
+    e_lse = max_abs(lse.cpu().numpy()[:, rows], ref_lse)
+    log(f"  n=4096 top-32: sel mismatch {cmp['mismatch']} (exempt {cmp['exempt']}), max|out| err {e_out:.3e}, "
+        f"max|lse| err {e_lse:.3e}")
+    assert e_out <= OUT_TOL["bf16"] and e_lse <= LSE_TOL["bf16"]
