@@ -155,10 +155,11 @@ hipError_t launch_pool(const void* k, bool is_f32, float* kbar, bf16* pieces, in
                        hipStream_t stream, int mode, const float* weights) {
   const int n = static_cast<int>(N / B);
   // Heads per workgroup: the largest of 8, 4, 2, 1 that divides H (longer
-  // contiguous runs per token row) while leaving at least 1024 workgroups to
-  // keep enough loads in flight, and with a row pass of at most 256 threads.
+  // contiguous runs per token row) while leaving at least 512 workgroups (two
+  // per CU) to keep enough loads in flight, and with a row pass of at most 256
+  // threads (measured at 32 heads: 512 workgroups of 4 heads beat 1024 of 2).
   int hg = 8;
-  while (hg > 1 && (H % hg != 0 || hg * (D / 8) > 256 || static_cast<int64_t>(n) * (H / hg) < 1024)) hg /= 2;
+  while (hg > 1 && (H % hg != 0 || hg * (D / 8) > 256 || static_cast<int64_t>(n) * (H / hg) < 512)) hg /= 2;
   dim3 grid(n, H / hg);
   if (is_f32) {
     const float* kf = static_cast<const float*>(k);
