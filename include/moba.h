@@ -1,6 +1,7 @@
 /*
- * libmoba — MoBA (Mixture of Block Attention) causal prefill forward pass for
- * AMD Instinct MI355X (gfx950).
+ * libmoba — MoBA (Mixture of Block Attention) for AMD Instinct MI355X (gfx950):
+ * the causal prefill forward pass, its backward pass, the decode step, pooling
+ * variants with dynamic k, and packed (varlen) batches.
  *
  * The method (Moonshot AI's MoBA as described by the pomoai MoBA overview,
  * "核心原理" steps 1-3, and by the 智东西 report, section 二):
@@ -15,7 +16,8 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- *   One sequence (batch 1), H query heads and H key/value heads.
+ *   One sequence (batch 1; the *_varlen calls pack several), H query heads and
+ *   H key/value heads.
  *   q, k, v, out : device pointers, row-major [N][H][D] (token, head, dim),
  *                  bf16 for the plain entry points and fp32 for the *_f32 twins.
  *   lse          : device pointer, fp32 [H][N], natural log of the softmax
@@ -25,7 +27,8 @@
  *                  query has fewer than topk eligible blocks (j + 1 < topk).
  *   kbar         : device pointer, fp32 [H][n][D], block mean keys.
  *   topk         : blocks per query including the forced current block;
- *                  topk >= n selects every past block (full causal attention).
+ *                  topk >= n selects every past block (full causal attention;
+ *                  the bf16 prefill and backward then run a dense causal path).
  *   stream       : HIP stream the work is enqueued on (0 = the null stream).
  *   Selection ties (equal fp32 scores) go to the lower block index.
  *
