@@ -13,15 +13,17 @@ past-block attention launch), and the fp64 oracle timed on the host on a
 sample of query rows.
 
 A ``dense`` object times the same inputs with top_k = n (every block kept:
-causal attention, counted as N(N+1)/2 pairs per head). A ``varlen`` object times the same tokens as 8 packed sequences of N/8 tokens.
-A ``pooling`` object times the prefill with max and weighted block pooling.
-A ``backward`` object times ``moba_prefill_bwd`` (dQ, dK, dV for a seeded
-upstream gradient) on the same inputs, effective TFLOP/s counted as 2.5x the
-forward's attended-pair work. A ``decode`` object beside it times ``moba_decode_fwd`` for the newest token of
-the same K/V cache (block means kept from the prefill, as a generation loop
-keeps them): once gated with the workload's top-k and once with top-k above
-the block count (full attention over the whole cache). Decode reads 4*D bytes
-of keys and values per attended key and head, so it is priced against HBM.
+causal attention, counted as N(N+1)/2 pairs per head). A ``varlen`` object
+times the same tokens as 8 packed sequences of N/8 tokens. A ``pooling``
+object times the prefill with max and weighted block pooling. A ``backward``
+object times ``moba_prefill_bwd`` (dQ, dK, dV for a seeded upstream gradient)
+on the same inputs, effective TFLOP/s counted as 2.5x the forward's
+attended-pair work. A ``decode`` object times ``moba_decode_fwd`` for the
+newest token of the same K/V cache (block means kept from the prefill, as a
+generation loop keeps them): once gated with the workload's top-k and once
+with top-k above the block count (full attention over the whole cache).
+Decode reads 4*D bytes of keys and values per attended key and head, so it is
+priced against HBM.
 """
 
 from __future__ import annotations
@@ -288,7 +290,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by head with no communication; see the design notes)", file=sys.stderr)
+              "(the path shards by head with no communication between GPUs)", file=sys.stderr)
         sys.exit(2)
 
     import torch
