@@ -28,7 +28,7 @@ What it computes (one sequence, H heads, head size D, block size B, n = N/B):
    (pomoai overview step 3; 智东西 section 二 steps 3-5) are only a faster route
    to this one softmax, so the oracle evaluates the softmax directly.
 
-Readings of points the pages leave open (each one is listed in the design notes):
+Readings of points the pages leave open:
 
 * top_k counts the forced current block (k blocks in total; the configuration
   section of the wzjinhao.cn article says a token sees exactly k blocks and
