@@ -263,25 +263,32 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
       // S and dP for key group kg and queries 32 wh .. 32 wh + 31 of the tile.
       const f32x16 s = rows_by_regs<D>(qt + wh * 32 * L::kRow + row_lane, kr);
       const f32x16 dp = rows_by_regs<D>(dt + wh * 32 * L::kRow + row_lane, vr);
+      auto softmax = [&](auto masked) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int rq = wh * 32 + 8 * g4 + 4 * half;
-        const float4 l4 = *reinterpret_cast<const float4*>(&s_lse[buf][rq]);
-        const float4 d4 = *reinterpret_cast<const float4*>(&s_del[buf][rq]);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-        bf16x4 p4, ds4;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int rq = wh * 32 + 8 * g4 + 4 * half;
+          const float4 l4 = *reinterpret_cast<const float4*>(&s_lse[buf][rq]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&s_del[buf][rq]);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+          bf16x4 p4, ds4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g4 + e;
-          float pr = __builtin_amdgcn_exp2f(fmaf(s[r], a.scale_log2, -lv[e]));
-          if (own && kofs + col > q0 + rq + e) pr = 0.f;   // key after the query
-          p4[e] = static_cast<bf16>(pr);
-          ds4[e] = static_cast<bf16>(pr * (dp[r] - dv[e]));
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g4 + e;
+            float pr = __builtin_amdgcn_exp2f(fmaf(s[r], a.scale_log2, -lv[e]));
+            if constexpr (decltype(masked)::value)
+              if (kofs + col > q0 + rq + e) pr = 0.f;   // key after the query
+            p4[e] = static_cast<bf16>(pr);
+            ds4[e] = static_cast<bf16>(pr * (dp[r] - dv[e]));
+          }
+          *reinterpret_cast<bf16x4*>(xp + 2 * rq) = p4;
+          *reinterpret_cast<bf16x4*>(xp + 4 * kX + 2 * rq) = ds4;
         }
-        *reinterpret_cast<bf16x4*>(xp + 2 * rq) = p4;
-        *reinterpret_cast<bf16x4*>(xp + 4 * kX + 2 * rq) = ds4;
-      }
+      };
+      // Only own tiles whose (key group, query half) square crosses the
+      // diagonal hold keys after a query; the rest skip the mask (uniform branch).
+      if (own && kofs + 31 > q0 + 32 * wh) softmax(std::true_type{});
+      else softmax(std::false_type{});
     }
     __syncthreads();
     if (active && !(own && kofs > q0 + kBwdQTile - 1)) {   // (all P = 0 otherwise)
@@ -424,12 +431,19 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
       const f32x16 s = rows_by_regs<D>(kt + kh * 32 * L::kRow + row_lane, qr);
       const f32x16 dp = rows_by_regs<D>(vt + kh * 32 * L::kRow + row_lane, dr);
       f32x16 ds;
+      auto softmax = [&](auto masked) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pr = __builtin_amdgcn_exp2f(fmaf(s[r], a.scale_log2, -lse2));
-        if (kOwn && kbase + 8 * (r >> 2) + 4 * half + (r & 3) > t) pr = 0.f;   // key after the query
-        ds[r] = pr * (dp[r] - del);
-      }
+        for (int r = 0; r < 16; ++r) {
+          float pr = __builtin_amdgcn_exp2f(fmaf(s[r], a.scale_log2, -lse2));
+          if constexpr (decltype(masked)::value)
+            if (kbase + 8 * (r >> 2) + 4 * half + (r & 3) > t) pr = 0.f;   // key after the query
+          ds[r] = pr * (dp[r] - del);
+        }
+      };
+      // Own items: only a key half that crosses the diagonal of the wave's
+      // queries holds keys after a query (uniform branch).
+      if (kOwn && kbase + 31 > t0 + 32 * w) softmax(std::true_type{});
+      else softmax(std::false_type{});
       bf16x8 dsp[2];
       pack16(ds, dsp);
 #pragma unroll
