@@ -179,22 +179,24 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) adv[dc][r] = adk[dc][r] = 0.f;
 
-  // Tile rows: the token of row r of tile i (-1: no query).
-  auto token = [&](int i, int r) -> int64_t {
+  // Tile rows: the token of row r of tile i (-1: no query). Tokens stay 32-bit
+  // (N < 2^31): a widened list entry would make the compiler wait for the
+  // entry, and with it for every older load of the tile, right after the lookup.
+  auto token = [&](int i, int r) -> int {
     if (i >= t_all) return -1;
     if (i < t_past) {
       const int e = kBwdQTile * i + r;
       return e < llen ? a.qidx[lstart + e] : -1;
     }
     const int o = own0 + kBwdQTile * (i - t_past) + r;
-    return o < a.B ? static_cast<int64_t>(b) * a.B + o : -1;
+    return o < a.B ? b * a.B + o : -1;
   };
   // Loader: 64 rows x kChunks 16-byte chunks of Q and dO; the rows' tokens are
   // looked up one tile ahead of the row loads.
   constexpr int kPer = kBwdQTile * L::kChunks / 512;
   uint4 pq[kPer], pd[kPer];
-  int64_t tok[kPer];
-  int64_t tok_l = -1;
+  int tok[kPer];
+  int tok_l = -1;
   float plse = INFINITY, pdel = 0.f;
   auto lookup = [&](int i) {
 #pragma unroll
@@ -206,13 +208,13 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
     for (int u = 0; u < kPer; ++u) {
       const int ch = (tid + 512 * u) % L::kChunks;
       const bool ok = tok[u] >= 0;
-      const int64_t off = (ok ? tok[u] : 0) * row_el + hd + 8 * ch;
+      const int64_t off = static_cast<int64_t>(ok ? tok[u] : 0) * row_el + hd + 8 * ch;
       pq[u] = ok ? ld16(a.q + off) : make_uint4(0, 0, 0, 0);
       pd[u] = ok ? ld16(a.dout + off) : make_uint4(0, 0, 0, 0);
     }
     if (tid < kBwdQTile) {
       const bool ok = tok_l >= 0;
-      plse = ok ? a.lse[static_cast<int64_t>(h) * a.N + tok_l] * kBwdLog2e : INFINITY;
+      plse = ok ? a.lse[static_cast<int64_t>(h) * a.N + tok_l] : INFINITY;   // scaled at the commit
       pdel = ok ? a.delta[static_cast<int64_t>(h) * a.N + tok_l] : 0.f;
     }
   };
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
       *reinterpret_cast<uint4*>(&tiles[buf][L::kTile + r * L::kRow + 16 * ch]) = pd[u];
     }
     if (tid < kBwdQTile) {
-      s_lse[buf][tid] = plse;
+      s_lse[buf][tid] = plse * kBwdLog2e;
       s_del[buf][tid] = pdel;
     }
   };
