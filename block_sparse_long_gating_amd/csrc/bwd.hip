@@ -387,6 +387,16 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[dc][r] = 0.f;
 
+  // Own items: the list positions of the query's first two past partials are
+  // requested now and used after the key loop.
+  int inv0 = 0, inv1 = 0;
+  if (kOwn && valid) {
+    const int np = kept_past(b, a.blo != nullptr ? a.blo[b] : 0, a.topk);
+    const int64_t ibase = (static_cast<int64_t>(h) * a.N + t) * a.lmax;
+    if (np > 0) inv0 = a.inv[ibase];
+    if (np > 1) inv1 = a.inv[ibase + 1];
+  }
+
   // Key tiles of block b; the own block stops at the item's last query.
   const int64_t kb0 = static_cast<int64_t>(b) * a.B;
   const int nkeys = kOwn ? static_cast<int>(t0 - kb0) + count : a.B;
@@ -434,11 +444,12 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
       const f32x16 dp = rows_by_regs<D>(vt + kh * 32 * L::kRow + row_lane, dr);
       f32x16 ds;
       auto softmax = [&](auto masked) {
+        const int rel = masked ? static_cast<int>(t - kbase) - 4 * half : 0;   // |t - kbase| < B
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float pr = __builtin_amdgcn_exp2f(fmaf(s[r], a.scale_log2, -lse2));
           if constexpr (decltype(masked)::value)
-            if (kbase + 8 * (r >> 2) + 4 * half + (r & 3) > t) pr = 0.f;   // key after the query
+            if (8 * (r >> 2) + (r & 3) > rel) pr = 0.f;   // key after the query
           ds[r] = pr * (dp[r] - del);
         }
       };
@@ -476,22 +487,39 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
             make_float4(acc[dc][4 * g4], acc[dc][4 * g4 + 1], acc[dc][4 * g4 + 2], acc[dc][4 * g4 + 3]);
     return;
   }
-  // Own block: add the query's past partials, scale, write dQ.
-  const int j = b;
-  const int np = kept_past(j, a.blo != nullptr ? a.blo[j] : 0, a.topk);
+  // Own block: add the query's past partials (two rows in flight at a time, in
+  // list order), scale, write dQ.
+  const int np = kept_past(b, a.blo != nullptr ? a.blo[b] : 0, a.topk);
   const int64_t ibase = (static_cast<int64_t>(h) * a.N + t) * a.lmax;
-  for (int s2 = 0; s2 < np; ++s2) {
-    const float* src = a.part_dq + static_cast<int64_t>(a.inv[ibase + s2]) * D;
+  for (int s2 = 0; s2 < np; s2 += 2) {
+    const bool two = s2 + 1 < np;
+    const int r0 = s2 == 0 ? inv0 : a.inv[ibase + s2];
+    const int r1 = !two ? r0 : s2 == 0 ? inv1 : a.inv[ibase + s2 + 1];
+    const float* src0 = a.part_dq + static_cast<int64_t>(r0) * D;
+    const float* src1 = a.part_dq + static_cast<int64_t>(r1) * D;
+    float4 x0[D / 8], x1[D / 8];
 #pragma unroll
-    for (int dc = 0; dc < D / 32; ++dc)
+    for (int c = 0; c < D / 8; ++c) {
+      const int d0 = 32 * (c >> 2) + 8 * (c & 3) + 4 * half;
+      x0[c] = *reinterpret_cast<const float4*>(src0 + d0);
+      x1[c] = *reinterpret_cast<const float4*>(src1 + d0);
+    }
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const float4 x = *reinterpret_cast<const float4*>(src + 32 * dc + 8 * g4 + 4 * half);
-        acc[dc][4 * g4] += x.x;
-        acc[dc][4 * g4 + 1] += x.y;
-        acc[dc][4 * g4 + 2] += x.z;
-        acc[dc][4 * g4 + 3] += x.w;
+    for (int c = 0; c < D / 8; ++c) {
+      acc[c >> 2][4 * (c & 3)] += x0[c].x;
+      acc[c >> 2][4 * (c & 3) + 1] += x0[c].y;
+      acc[c >> 2][4 * (c & 3) + 2] += x0[c].z;
+      acc[c >> 2][4 * (c & 3) + 3] += x0[c].w;
+    }
+    if (two) {
+#pragma unroll
+      for (int c = 0; c < D / 8; ++c) {
+        acc[c >> 2][4 * (c & 3)] += x1[c].x;
+        acc[c >> 2][4 * (c & 3) + 1] += x1[c].y;
+        acc[c >> 2][4 * (c & 3) + 2] += x1[c].z;
+        acc[c >> 2][4 * (c & 3) + 3] += x1[c].w;
       }
+    }
   }
   bf16* dq = a.dq + t * row_el + hd;
 #pragma unroll
