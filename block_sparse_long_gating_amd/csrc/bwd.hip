@@ -98,6 +98,28 @@ __device__ __forceinline__ void pack16(const f32x16& x, bf16x8 (&p)[2]) {
 
 __device__ __forceinline__ uint4 ld16(const bf16* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// Scalar load of work item idx (wave-uniform), waited for in the same
+// statement. The list was written by an earlier kernel and is read-only here;
+// inside a loop that also stores, the compiler would use a vector load, and
+// waiting for that would wait for every vector load and store in flight.
+__device__ __forceinline__ WorkItem load_item(const WorkItem* items, int idx) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const uint64_t p = reinterpret_cast<uint64_t>(items + __builtin_amdgcn_readfirstlane(idx));
+  // readfirstlane works on 32-bit ints; each half goes through uint32_t so that
+  // widening never sign-extends.
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(p))));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(p >> 32))));
+  const uint64_t addr = (static_cast<uint64_t>(hi) << 32) | lo;
+  i32x4 v;
+  asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(addr));
+  WorkItem it;
+  it.h = v.x;
+  it.b = v.y;
+  it.start = v.z;
+  it.count = v.w;
+  return it;
+}
+
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
   const int kl = a.D / 8;                          // lanes per row
   const int rows = 256 / kl;
@@ -346,191 +368,235 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __align__(16) char tiles[2][2 * L::kTile];   // [buffer][K tile, V tile]
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
-  int h, b, count;
-  int64_t t0 = 0;         // own items: first query
-  int lstart = 0;         // past items: first list position
-  if (kOwn) {
-    // Within a block, later query tiles (more keys) are dispatched first.
-    const int per = (a.B + kAttnTile - 1) / kAttnTile;
-    const int x = per - 1 - static_cast<int>(blockIdx.x % per);
-    const int rest = blockIdx.x / per;
-    h = rest % a.H;
-    b = rest / a.H;
-    t0 = static_cast<int64_t>(b) * a.B + static_cast<int64_t>(x) * kAttnTile;
-    count = min(kAttnTile, a.B - x * kAttnTile);
-  } else {
-    if (static_cast<int>(blockIdx.x) >= a.counters[0]) return;
-    const WorkItem it = a.items[blockIdx.x];
-    h = it.h;
-    b = it.b;
-    lstart = it.start;
-    count = it.count;
-  }
-  const int64_t hd = static_cast<int64_t>(h) * D;
-  const int64_t row_el = static_cast<int64_t>(a.H) * D;
-  const int pos = 32 * w + col;                    // this lane's query inside the item
-  const bool valid = pos < count;
-  int64_t t = 0;
-  if (valid) t = kOwn ? t0 + pos : a.qidx[lstart + pos];
-  bf16x8 qr[D / 16], dr[D / 16];
-#pragma unroll
-  for (int cc = 0; cc < D / 16; ++cc) {
-    const int64_t off = t * row_el + hd + 16 * cc + 8 * half;
-    qr[cc] = valid ? __builtin_bit_cast(bf16x8, ld16(a.q + off)) : bf16x8{};
-    dr[cc] = valid ? __builtin_bit_cast(bf16x8, ld16(a.dout + off)) : bf16x8{};
-  }
-  const float lse2 = valid ? a.lse[static_cast<int64_t>(h) * a.N + t] * kBwdLog2e : INFINITY;
-  const float del = valid ? a.delta[static_cast<int64_t>(h) * a.N + t] : 0.f;
-  f32x16 acc[D / 32];
-#pragma unroll
-  for (int dc = 0; dc < D / 32; ++dc)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[dc][r] = 0.f;
-
-  // Own items: the list positions of the query's first two past partials are
-  // requested now and used after the key loop.
-  int inv0 = 0, inv1 = 0;
-  if (kOwn && valid) {
-    const int np = kept_past(b, a.blo != nullptr ? a.blo[b] : 0, a.topk);
-    const int64_t ibase = (static_cast<int64_t>(h) * a.N + t) * a.lmax;
-    if (np > 0) inv0 = a.inv[ibase];
-    if (np > 1) inv1 = a.inv[ibase + 1];
-  }
-
-  // Key tiles of block b; the own block stops at the item's last query.
-  const int64_t kb0 = static_cast<int64_t>(b) * a.B;
-  const int nkeys = kOwn ? static_cast<int>(t0 - kb0) + count : a.B;
-  const int ntiles = (nkeys + kBwdKTile - 1) / kBwdKTile;
-  constexpr int kPer = kBwdKTile * L::kChunks / 512;
-  uint4 pk[kPer], pv[kPer];
-  auto fetch = [&](int i) {
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int idx = tid + 512 * u;
-      const int r = idx / L::kChunks, ch = idx % L::kChunks;
-      const int64_t off = (kb0 + kBwdKTile * i + r) * row_el + hd + 8 * ch;   // always inside block b
-      pk[u] = ld16(a.k + off);
-      pv[u] = ld16(a.v + off);
+  const int pos = 32 * w + col;                    // this lane's query inside an item
+  // Past items: persistent workgroups on a static, XCD-aware schedule (XCD x =
+  // blockIdx % 8 takes a contiguous eighth of the item list and its
+  // workgroups every (G/8)-th item of it), so the items of one key block run
+  // on one XCD at the same time and share its K/V rows in that XCD's L2. The
+  // list entries of a workgroup's next item are requested at the start of the
+  // current one. Own items: one item per workgroup.
+  int ii = 0, iend = 1, istep = 1;
+  int tok_next = 0;
+  if (!kOwn) {
+    const int nitems = a.counters[0];
+    const int G = static_cast<int>(gridDim.x);
+    if (G % kXcds == 0) {
+      const int x = static_cast<int>(blockIdx.x) % kXcds;
+      ii = static_cast<int>(static_cast<int64_t>(nitems) * x / kXcds) + static_cast<int>(blockIdx.x) / kXcds;
+      iend = static_cast<int>(static_cast<int64_t>(nitems) * (x + 1) / kXcds);
+      istep = G / kXcds;
+    } else {
+      ii = static_cast<int>(blockIdx.x);
+      iend = nitems;
+      istep = G;
     }
-  };
-  auto commit = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int idx = tid + 512 * u;
-      const int r = idx / L::kChunks, ch = idx % L::kChunks;
-      *reinterpret_cast<uint4*>(&tiles[buf][r * L::kRow + 16 * ch]) = pk[u];
-      *reinterpret_cast<uint4*>(&tiles[buf][L::kTile + r * L::kRow + 16 * ch]) = pv[u];
+    if (ii >= iend) return;
+    const WorkItem it = load_item(a.items, ii);
+    if (pos < it.count) tok_next = a.qidx[it.start + pos];
+  }
+  for (;;) {
+    int h, b, count;
+    int64_t t0 = 0;         // own items: first query
+    int lstart = 0;         // past items: first list position
+    if (kOwn) {
+      // Within a block, later query tiles (more keys) are dispatched first.
+      const int per = (a.B + kAttnTile - 1) / kAttnTile;
+      const int x = per - 1 - static_cast<int>(blockIdx.x % per);
+      const int rest = blockIdx.x / per;
+      h = rest % a.H;
+      b = rest / a.H;
+      t0 = static_cast<int64_t>(b) * a.B + static_cast<int64_t>(x) * kAttnTile;
+      count = min(kAttnTile, a.B - x * kAttnTile);
+    } else {
+      const WorkItem it = load_item(a.items, ii);
+      h = it.h;
+      b = it.b;
+      lstart = it.start;
+      count = it.count;
     }
-  };
-  const int tg = lane >> 4, te = (lane >> 2) & 3, tq = lane & 3;
-  const int row_lane = col * L::kRow + 16 * half;
-  const int tr_lane = (4 * (tg >> 1) + te) * L::kRow + 2 * (16 * (tg & 1) + 4 * tq);
-  // This wave's last query (wave-uniform): key halves after it are all masked
-  // (own items), and a wave without queries has nothing to add.
-  const int64_t wlast = 32 * w < count ? (kOwn ? t0 + min(32 * w + 31, count - 1) : INT64_MAX) : -1;
-  fetch(0);
-  commit(0);
-  __syncthreads();
-  for (int i = 0; i < ntiles; ++i) {
-    const int buf = i & 1;
-    if (i + 1 < ntiles) fetch(i + 1);
-    const char* kt = tiles[buf];
-    const char* vt = tiles[buf] + L::kTile;
+    const int64_t hd = static_cast<int64_t>(h) * D;
+    const int64_t row_el = static_cast<int64_t>(a.H) * D;
+    const bool valid = pos < count;
+    int64_t t = 0;
+    if (valid) t = kOwn ? t0 + pos : tok_next;
+    bf16x8 qr[D / 16], dr[D / 16];
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const int64_t kbase = kb0 + kBwdKTile * i + 32 * kh;
-      if (kbase > wlast) continue;
-      const f32x16 s = rows_by_regs<D>(kt + kh * 32 * L::kRow + row_lane, qr);
-      const f32x16 dp = rows_by_regs<D>(vt + kh * 32 * L::kRow + row_lane, dr);
-      f32x16 ds;
-      auto softmax = [&](auto masked) {
-        const int rel = masked ? static_cast<int>(t - kbase) - 4 * half : 0;   // |t - kbase| < B
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pr = __builtin_amdgcn_exp2f(fmaf(s[r], a.scale_log2, -lse2));
-          if constexpr (decltype(masked)::value)
-            if (8 * (r >> 2) + (r & 3) > rel) pr = 0.f;   // key after the query
-          ds[r] = pr * (dp[r] - del);
-        }
-      };
-      // Own items: only a key half that crosses the diagonal of the wave's
-      // queries holds keys after a query (uniform branch).
-      if (kOwn && kbase + 31 > t0 + 32 * w) softmax(std::true_type{});
-      else softmax(std::false_type{});
-      bf16x8 dsp[2];
-      pack16(ds, dsp);
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const int roff = (kh * 32 + 16 * g) * L::kRow + tr_lane;
-#pragma unroll
-        for (int dc = 0; dc < D / 32; ++dc) {
-          const bf16x8 ktr = tr_operand<L::kRow>(kt + roff + 64 * dc);
-          acc[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktr, dsp[g], acc[dc], 0, 0, 0);
-        }
+    for (int cc = 0; cc < D / 16; ++cc) {
+      const int64_t off = t * row_el + hd + 16 * cc + 8 * half;
+      qr[cc] = valid ? __builtin_bit_cast(bf16x8, ld16(a.q + off)) : bf16x8{};
+      dr[cc] = valid ? __builtin_bit_cast(bf16x8, ld16(a.dout + off)) : bf16x8{};
+    }
+    float lse_raw = valid ? a.lse[static_cast<int64_t>(h) * a.N + t] : INFINITY;   // scaled below
+    const float del = valid ? a.delta[static_cast<int64_t>(h) * a.N + t] : 0.f;
+    if (!kOwn) {
+      // The next item's list entries, after this item's row loads.
+      tok_next = 0;
+      if (ii + istep < iend) {
+        const WorkItem it = load_item(a.items, ii + istep);
+        if (pos < it.count) tok_next = a.qidx[it.start + pos];
       }
     }
-    __syncthreads();
-    if (i + 1 < ntiles) {
-      commit(buf ^ 1);
-      __syncthreads();
-    }
-  }
-  if (!valid) return;
-  // dQᵀ rows are dims 32 dc + 8 g4 + 4 half + 0..3 of this lane's query.
-  if (!kOwn) {
-    float* dst = a.part_dq + static_cast<int64_t>(lstart + pos) * D;
+    f32x16 acc[D / 32];
 #pragma unroll
     for (int dc = 0; dc < D / 32; ++dc)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4)
-        *reinterpret_cast<float4*>(dst + 32 * dc + 8 * g4 + 4 * half) =
-            make_float4(acc[dc][4 * g4], acc[dc][4 * g4 + 1], acc[dc][4 * g4 + 2], acc[dc][4 * g4 + 3]);
-    return;
-  }
-  // Own block: add the query's past partials (two rows in flight at a time, in
-  // list order), scale, write dQ.
-  const int np = kept_past(b, a.blo != nullptr ? a.blo[b] : 0, a.topk);
-  const int64_t ibase = (static_cast<int64_t>(h) * a.N + t) * a.lmax;
-  for (int s2 = 0; s2 < np; s2 += 2) {
-    const bool two = s2 + 1 < np;
-    const int r0 = s2 == 0 ? inv0 : a.inv[ibase + s2];
-    const int r1 = !two ? r0 : s2 == 0 ? inv1 : a.inv[ibase + s2 + 1];
-    const float* src0 = a.part_dq + static_cast<int64_t>(r0) * D;
-    const float* src1 = a.part_dq + static_cast<int64_t>(r1) * D;
-    float4 x0[D / 8], x1[D / 8];
+      for (int r = 0; r < 16; ++r) acc[dc][r] = 0.f;
+
+    int inv0 = 0, inv1 = 0;   // own items: list positions of the first two past partials
+
+    // Key tiles of block b; the own block stops at the item's last query.
+    const int64_t kb0 = static_cast<int64_t>(b) * a.B;
+    const int nkeys = kOwn ? static_cast<int>(t0 - kb0) + count : a.B;
+    const int ntiles = (nkeys + kBwdKTile - 1) / kBwdKTile;
+    constexpr int kPer = kBwdKTile * L::kChunks / 512;
+    uint4 pk[kPer], pv[kPer];
+    auto fetch = [&](int i) {
 #pragma unroll
-    for (int c = 0; c < D / 8; ++c) {
-      const int d0 = 32 * (c >> 2) + 8 * (c & 3) + 4 * half;
-      x0[c] = *reinterpret_cast<const float4*>(src0 + d0);
-      x1[c] = *reinterpret_cast<const float4*>(src1 + d0);
+      for (int u = 0; u < kPer; ++u) {
+        const int idx = tid + 512 * u;
+        const int r = idx / L::kChunks, ch = idx % L::kChunks;
+        const int64_t off = (kb0 + kBwdKTile * i + r) * row_el + hd + 8 * ch;   // always inside block b
+        pk[u] = ld16(a.k + off);
+        pv[u] = ld16(a.v + off);
+      }
+    };
+    auto commit = [&](int buf) {
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int idx = tid + 512 * u;
+        const int r = idx / L::kChunks, ch = idx % L::kChunks;
+        *reinterpret_cast<uint4*>(&tiles[buf][r * L::kRow + 16 * ch]) = pk[u];
+        *reinterpret_cast<uint4*>(&tiles[buf][L::kTile + r * L::kRow + 16 * ch]) = pv[u];
+      }
+    };
+    const int tg = lane >> 4, te = (lane >> 2) & 3, tq = lane & 3;
+    const int row_lane = col * L::kRow + 16 * half;
+    const int tr_lane = (4 * (tg >> 1) + te) * L::kRow + 2 * (16 * (tg & 1) + 4 * tq);
+    // This wave's last query (wave-uniform): key halves after it are all masked
+    // (own items), and a wave without queries has nothing to add.
+    const int64_t wlast = 32 * w < count ? (kOwn ? t0 + min(32 * w + 31, count - 1) : INT64_MAX) : -1;
+    fetch(0);
+    if (kOwn && valid) {
+      // Requested after the first tile's loads (the block's sequence start may
+      // have to arrive first) and used after the key loop.
+      const int np = kept_past(b, a.blo != nullptr ? a.blo[b] : 0, a.topk);
+      const int64_t ibase = (static_cast<int64_t>(h) * a.N + t) * a.lmax;
+      if (np > 0) inv0 = a.inv[ibase];
+      if (np > 1) inv1 = a.inv[ibase + 1];
     }
+    commit(0);
+    __syncthreads();
+    // Scaled only here, where every load above has been waited for: a multiply
+    // right after the load would hold the first tile's loads back until then
+    // (the empty asm keeps the compiler from moving it there).
+    asm volatile("" : "+v"(lse_raw));
+    const float lse2 = lse_raw * kBwdLog2e;
+    for (int i = 0; i < ntiles; ++i) {
+      const int buf = i & 1;
+      if (i + 1 < ntiles) fetch(i + 1);
+      const char* kt = tiles[buf];
+      const char* vt = tiles[buf] + L::kTile;
 #pragma unroll
-    for (int c = 0; c < D / 8; ++c) {
-      acc[c >> 2][4 * (c & 3)] += x0[c].x;
-      acc[c >> 2][4 * (c & 3) + 1] += x0[c].y;
-      acc[c >> 2][4 * (c & 3) + 2] += x0[c].z;
-      acc[c >> 2][4 * (c & 3) + 3] += x0[c].w;
-    }
-    if (two) {
+      for (int kh = 0; kh < 2; ++kh) {
+        const int64_t kbase = kb0 + kBwdKTile * i + 32 * kh;
+        if (kbase > wlast) continue;
+        const f32x16 s = rows_by_regs<D>(kt + kh * 32 * L::kRow + row_lane, qr);
+        const f32x16 dp = rows_by_regs<D>(vt + kh * 32 * L::kRow + row_lane, dr);
+        f32x16 ds;
+        auto softmax = [&](auto masked) {
+          const int rel = masked ? static_cast<int>(t - kbase) - 4 * half : 0;   // |t - kbase| < B
 #pragma unroll
-      for (int c = 0; c < D / 8; ++c) {
-        acc[c >> 2][4 * (c & 3)] += x1[c].x;
-        acc[c >> 2][4 * (c & 3) + 1] += x1[c].y;
-        acc[c >> 2][4 * (c & 3) + 2] += x1[c].z;
-        acc[c >> 2][4 * (c & 3) + 3] += x1[c].w;
+          for (int r = 0; r < 16; ++r) {
+            float pr = __builtin_amdgcn_exp2f(fmaf(s[r], a.scale_log2, -lse2));
+            if constexpr (decltype(masked)::value)
+              if (8 * (r >> 2) + (r & 3) > rel) pr = 0.f;   // key after the query
+            ds[r] = pr * (dp[r] - del);
+          }
+        };
+        // Own items: only a key half that crosses the diagonal of the wave's
+        // queries holds keys after a query (uniform branch).
+        if (kOwn && kbase + 31 > t0 + 32 * w) softmax(std::true_type{});
+        else softmax(std::false_type{});
+        bf16x8 dsp[2];
+        pack16(ds, dsp);
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const int roff = (kh * 32 + 16 * g) * L::kRow + tr_lane;
+#pragma unroll
+          for (int dc = 0; dc < D / 32; ++dc) {
+            const bf16x8 ktr = tr_operand<L::kRow>(kt + roff + 64 * dc);
+            acc[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktr, dsp[g], acc[dc], 0, 0, 0);
+          }
+        }
+      }
+      __syncthreads();
+      if (i + 1 < ntiles) {
+        commit(buf ^ 1);
+        __syncthreads();
       }
     }
-  }
-  bf16* dq = a.dq + t * row_el + hd;
+    // dQᵀ rows are dims 32 dc + 8 g4 + 4 half + 0..3 of this lane's query.
+    if (!kOwn) {
+      if (valid) {
+        float* dst = a.part_dq + static_cast<int64_t>(lstart + pos) * D;
 #pragma unroll
-  for (int dc = 0; dc < D / 32; ++dc)
+        for (int dc = 0; dc < D / 32; ++dc)
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      bf16x4 v4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v4[e] = static_cast<bf16>(acc[dc][4 * g4 + e] * a.scale);
-      *reinterpret_cast<bf16x4*>(dq + 32 * dc + 8 * g4 + 4 * half) = v4;
+          for (int g4 = 0; g4 < 4; ++g4)
+            *reinterpret_cast<float4*>(dst + 32 * dc + 8 * g4 + 4 * half) =
+                make_float4(acc[dc][4 * g4], acc[dc][4 * g4 + 1], acc[dc][4 * g4 + 2], acc[dc][4 * g4 + 3]);
+      }
+      ii += istep;
+      if (ii >= iend) return;
+      continue;   // the loop's last barrier ended every wave's reads of the tiles
     }
+    if (!valid) return;
+    // Own block: add the query's past partials (two rows in flight at a time, in
+    // list order), scale, write dQ.
+    const int np = kept_past(b, a.blo != nullptr ? a.blo[b] : 0, a.topk);
+    const int64_t ibase = (static_cast<int64_t>(h) * a.N + t) * a.lmax;
+    for (int s2 = 0; s2 < np; s2 += 2) {
+      const bool two = s2 + 1 < np;
+      const int r0 = s2 == 0 ? inv0 : a.inv[ibase + s2];
+      const int r1 = !two ? r0 : s2 == 0 ? inv1 : a.inv[ibase + s2 + 1];
+      const float* src0 = a.part_dq + static_cast<int64_t>(r0) * D;
+      const float* src1 = a.part_dq + static_cast<int64_t>(r1) * D;
+      float4 x0[D / 8], x1[D / 8];
+#pragma unroll
+      for (int c = 0; c < D / 8; ++c) {
+        const int d0 = 32 * (c >> 2) + 8 * (c & 3) + 4 * half;
+        x0[c] = *reinterpret_cast<const float4*>(src0 + d0);
+        x1[c] = *reinterpret_cast<const float4*>(src1 + d0);
+      }
+#pragma unroll
+      for (int c = 0; c < D / 8; ++c) {
+        acc[c >> 2][4 * (c & 3)] += x0[c].x;
+        acc[c >> 2][4 * (c & 3) + 1] += x0[c].y;
+        acc[c >> 2][4 * (c & 3) + 2] += x0[c].z;
+        acc[c >> 2][4 * (c & 3) + 3] += x0[c].w;
+      }
+      if (two) {
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c) {
+          acc[c >> 2][4 * (c & 3)] += x1[c].x;
+          acc[c >> 2][4 * (c & 3) + 1] += x1[c].y;
+          acc[c >> 2][4 * (c & 3) + 2] += x1[c].z;
+          acc[c >> 2][4 * (c & 3) + 3] += x1[c].w;
+        }
+      }
+    }
+    bf16* dq = a.dq + t * row_el + hd;
+#pragma unroll
+    for (int dc = 0; dc < D / 32; ++dc)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = static_cast<bf16>(acc[dc][4 * g4 + e] * a.scale);
+        *reinterpret_cast<bf16x4*>(dq + 32 * dc + 8 * g4 + 4 * half) = v4;
+      }
+    return;
+  }
 }
 
 }  // namespace
@@ -541,13 +607,15 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
   bwd_delta_kernel<<<static_cast<unsigned>((rows + per - 1) / per), 256, 0, stream>>>(a);
   const unsigned kv_grid = static_cast<unsigned>(static_cast<int64_t>(a.n) * a.H * ((a.B + kBwdKeys - 1) / kBwdKeys));
   const unsigned own_grid = static_cast<unsigned>(static_cast<int64_t>(a.n) * a.H * ((a.B + kAttnTile - 1) / kAttnTile));
+  // dQ past items: one persistent workgroup per CU (one fits at a time).
+  const unsigned past_grid = static_cast<unsigned>(a.num_cus > 0 ? std::min<int64_t>(a.max_items, a.num_cus) : a.max_items);
   if (a.D == 128) {
     bwd_dkdv_kernel<128><<<kv_grid, 512, 0, stream>>>(a);
-    if (a.max_items > 0) bwd_dq_kernel<128, false><<<static_cast<unsigned>(a.max_items), 512, 0, stream>>>(a);
+    if (a.max_items > 0) bwd_dq_kernel<128, false><<<past_grid, 512, 0, stream>>>(a);
     bwd_dq_kernel<128, true><<<own_grid, 512, 0, stream>>>(a);
   } else {
     bwd_dkdv_kernel<64><<<kv_grid, 512, 0, stream>>>(a);
-    if (a.max_items > 0) bwd_dq_kernel<64, false><<<static_cast<unsigned>(a.max_items), 512, 0, stream>>>(a);
+    if (a.max_items > 0) bwd_dq_kernel<64, false><<<past_grid, 512, 0, stream>>>(a);
     bwd_dq_kernel<64, true><<<own_grid, 512, 0, stream>>>(a);
   }
   return hipGetLastError();

@@ -118,6 +118,7 @@ struct BwdArgs {
   int64_t N;
   int H, D, B, n, topk, lmax;
   int64_t max_items;
+  int num_cus;            // compute units of the device (0: unknown)
   int has_lists;        // 0: no query lists (every block kept; one block of N tokens)
   const int32_t* blo;   // per-block first block of its sequence (packed sequences), or nullptr
   float scale;          // 1 / sqrt(D)

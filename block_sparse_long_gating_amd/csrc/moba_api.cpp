@@ -404,6 +404,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* out, 
   a.lmax = p.lmax;
   a.max_items = p.lmax > 0 ? p.max_items : 0;
   a.has_lists = dense ? 0 : 1;
+  a.num_cus = st->num_cus;
   a.scale = 1.0f / std::sqrt(static_cast<float>(D));
   a.scale_log2 = 1.4426950408889634f / std::sqrt(static_cast<float>(D));
   hipError_t e = hipSuccess;
