@@ -21,11 +21,14 @@
 //                      the block's own later queries (causal mask), in
 //                      64-query tiles staged in LDS (double-buffered through
 //                      registers, list entries looked up a tile ahead). Eight
-//                      waves: wave w holds K and V of key group w % 4 (32
-//                      keys) in registers and computes, for query half w / 4,
+//                      waves in two kinds, one of each per SIMD, working on
+//                      consecutive tiles at the same time: waves 0-3 hold K
+//                      and V of key group w (32 keys) in registers and turn
+//                      tile i into
 //                        S = Q Kᵀ, dP = dO Vᵀ (queries on the rows), P, dS,
-//                      which go to LDS as bf16; then for dims half w / 4 and
-//                      the whole tile
+//                      which go to a double-buffered LDS exchange as bf16;
+//                      waves 4-7 add tile i - 1 into all D dims of key group
+//                      w - 4:
 //                        dVᵀ += dOᵀ P, dKᵀ += Qᵀ dS (dOᵀ, Qᵀ by transpose reads).
 //                      Each key is owned by one workgroup: no atomics.
 //   bwd_dq_kernel      query-stationary over the same work items as the
@@ -153,14 +156,13 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
   using L = BwdLay<D>;
   constexpr int kXRow = 2 * kBwdQTile + 8;         // P / dS exchange row (one key, 64 queries, bf16; 34 dwords: conflict-free)
   constexpr int kX = 32 * kXRow;                   // one key group
-  constexpr int kDH = D / 2;                       // dims accumulated per wave
   __shared__ __align__(16) char tiles[2][2 * L::kTile];   // [buffer][Q tile, dO tile]
-  __shared__ __align__(16) char xch[2][4 * kX];            // [P, dS][key group]
+  __shared__ __align__(16) char xch[2][2][4 * kX];         // [buffer][P, dS][key group]
   __shared__ __align__(16) float s_lse[2][kBwdQTile];
   __shared__ __align__(16) float s_del[2][kBwdQTile];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
-  const int kg = w & 3, wh = w >> 2;               // key group; query half (S, dP) and dims half (dK, dV)
+  const int kg = w & 3;                            // key group
   const int chunks = (a.B + kBwdKeys - 1) / kBwdKeys;
   // XCD-aware order: the chunks of one (head, block) run on one XCD at the same
   // time (they read the same query rows), consecutive (head, block) pairs go
@@ -186,20 +188,6 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
   const int64_t hd = static_cast<int64_t>(h) * D;
   const int64_t row_el = static_cast<int64_t>(a.H) * D;
 
-  bf16x8 kr[D / 16], vr[D / 16];
-  {
-    const int64_t kk = active ? key0 + col : 0;
-#pragma unroll
-    for (int cc = 0; cc < D / 16; ++cc) {
-      kr[cc] = __builtin_bit_cast(bf16x8, ld16(a.k + kk * row_el + hd + 16 * cc + 8 * half));
-      vr[cc] = __builtin_bit_cast(bf16x8, ld16(a.v + kk * row_el + hd + 16 * cc + 8 * half));
-    }
-  }
-  f32x16 adv[kDH / 32], adk[kDH / 32];
-#pragma unroll
-  for (int dc = 0; dc < kDH / 32; ++dc)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) adv[dc][r] = adk[dc][r] = 0.f;
 
   // Tile rows: the token of row r of tile i (-1: no query). Tokens stay 32-bit
   // (N < 2^31): a widened list entry would make the compiler wait for the
@@ -257,78 +245,132 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
   const int tg = lane >> 4, te = (lane >> 2) & 3, tq = lane & 3;
   const int row_lane = col * L::kRow + 16 * half;
   const int tr_lane = (4 * (tg >> 1) + te) * L::kRow + 2 * (16 * (tg & 1) + 4 * tq);
-  char* xp = xch[0] + kg * kX + col * kXRow;       // this lane's key row of P (dS: xch[1])
+  const int xrow = kg * kX + col * kXRow;          // this lane's key row in a P or dS exchange area
+  // Own tiles: block offset of tile i's first query.
+  auto tile_q0 = [&](int i) { return own0 + kBwdQTile * (i - t_past); };
   lookup(0);
   fetch();
   commit(0);
   lookup(1);
   __syncthreads();
-  for (int i = 0; i < t_all; ++i) {
-    const int buf = i & 1;
-    if (i + 1 < t_all) {
-      fetch();          // rows of tile i + 1 (tokens looked up last iteration)
-      lookup(i + 2);
+  // Pipeline step st (0 .. t_all): the rows of tile st + 1 are loaded into
+  // registers, waves 0-3 turn tile st into P and dS while waves 4-7 add tile
+  // st - 1 into dV and dK (so every SIMD holds one wave of each kind), then,
+  // after a barrier, tile st + 1 goes into the buffer that tile st - 1 held,
+  // and a second barrier publishes it. Both kinds of wave pass the same
+  // barriers: 2 (t_all + 1) each.
+  auto step_begin = [&](int st) {
+    if (st + 1 < t_all) {
+      fetch();          // rows of tile st + 1 (tokens looked up one step earlier)
+      lookup(st + 2);
     }
-    const char* qt = tiles[buf];
-    const char* dt = tiles[buf] + L::kTile;
-    const bool own = i >= t_past;
-    const int q0 = own0 + kBwdQTile * (i - t_past);   // own tiles: offset of the tile's first query
-    if (active && own && kofs > q0 + 32 * wh + 31) {
-      // Every key of the group comes after every query of the half: P = dS = 0.
-      const bf16x4 z4 = {static_cast<bf16>(0.f), static_cast<bf16>(0.f), static_cast<bf16>(0.f),
-                         static_cast<bf16>(0.f)};
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int rq = wh * 32 + 8 * g4 + 4 * half;
-        *reinterpret_cast<bf16x4*>(xp + 2 * rq) = z4;
-        *reinterpret_cast<bf16x4*>(xp + 4 * kX + 2 * rq) = z4;
-      }
-    } else if (active) {
-      // S and dP for key group kg and queries 32 wh .. 32 wh + 31 of the tile.
-      const f32x16 s = rows_by_regs<D>(qt + wh * 32 * L::kRow + row_lane, kr);
-      const f32x16 dp = rows_by_regs<D>(dt + wh * 32 * L::kRow + row_lane, vr);
-      auto softmax = [&](auto masked) {
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int rq = wh * 32 + 8 * g4 + 4 * half;
-          const float4 l4 = *reinterpret_cast<const float4*>(&s_lse[buf][rq]);
-          const float4 d4 = *reinterpret_cast<const float4*>(&s_del[buf][rq]);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-          bf16x4 p4, ds4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g4 + e;
-            float pr = __builtin_amdgcn_exp2f(fmaf(s[r], a.scale_log2, -lv[e]));
-            if constexpr (decltype(masked)::value)
-              if (kofs + col > q0 + rq + e) pr = 0.f;   // key after the query
-            p4[e] = static_cast<bf16>(pr);
-            ds4[e] = static_cast<bf16>(pr * (dp[r] - dv[e]));
-          }
-          *reinterpret_cast<bf16x4*>(xp + 2 * rq) = p4;
-          *reinterpret_cast<bf16x4*>(xp + 4 * kX + 2 * rq) = ds4;
-        }
-      };
-      // Only own tiles whose (key group, query half) square crosses the
-      // diagonal hold keys after a query; the rest skip the mask (uniform branch).
-      if (own && kofs + 31 > q0 + 32 * wh) softmax(std::true_type{});
-      else softmax(std::false_type{});
-    }
+  };
+  auto step_end = [&](int st) {
     __syncthreads();
-    if (active && !(own && kofs > q0 + kBwdQTile - 1)) {   // (all P = 0 otherwise)
-      // dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS for dims kDH wh .. and the whole tile.
+    if (st + 1 < t_all) commit((st + 1) & 1);
+    __syncthreads();
+  };
+  if (w < 4) {
+    // K and V of the key group in registers; per tile, S = Q Kᵀ and dP = dO Vᵀ
+    // (queries on the rows) for each 32-query half, then P and dS as bf16 into
+    // the tile's exchange buffer.
+    bf16x8 kr[D / 16], vr[D / 16];
+    {
+      const int64_t kk = active ? key0 + col : 0;
+#pragma unroll
+      for (int cc = 0; cc < D / 16; ++cc) {
+        kr[cc] = __builtin_bit_cast(bf16x8, ld16(a.k + kk * row_el + hd + 16 * cc + 8 * half));
+        vr[cc] = __builtin_bit_cast(bf16x8, ld16(a.v + kk * row_el + hd + 16 * cc + 8 * half));
+      }
+    }
+    for (int st = 0; st <= t_all; ++st) {
+      step_begin(st);
+      const int buf = st & 1;
+      const bool own = st >= t_past;
+      const int q0 = tile_q0(st);
+      // Nothing to do past the last tile, and nothing to write when every key
+      // of the group comes after every query of the tile (the consumer skips it).
+      if (active && st < t_all && !(own && kofs > q0 + kBwdQTile - 1)) {
+        const char* qt = tiles[buf];
+        const char* dt = tiles[buf] + L::kTile;
+        char* xp = xch[buf][0] + xrow;
+        char* xs = xch[buf][1] + xrow;
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh) {
+          if (own && kofs > q0 + 32 * qh + 31) {
+            // Every key of the group comes after every query of the half: P = dS = 0.
+            const bf16x4 z4 = {static_cast<bf16>(0.f), static_cast<bf16>(0.f), static_cast<bf16>(0.f),
+                               static_cast<bf16>(0.f)};
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const int rq = qh * 32 + 8 * g4 + 4 * half;
+              *reinterpret_cast<bf16x4*>(xp + 2 * rq) = z4;
+              *reinterpret_cast<bf16x4*>(xs + 2 * rq) = z4;
+            }
+            continue;
+          }
+          const f32x16 sc = rows_by_regs<D>(qt + qh * 32 * L::kRow + row_lane, kr);
+          const f32x16 dp = rows_by_regs<D>(dt + qh * 32 * L::kRow + row_lane, vr);
+          auto softmax = [&](auto masked) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const int rq = qh * 32 + 8 * g4 + 4 * half;
+              const float4 l4 = *reinterpret_cast<const float4*>(&s_lse[buf][rq]);
+              const float4 d4 = *reinterpret_cast<const float4*>(&s_del[buf][rq]);
+              const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+              const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+              bf16x4 p4, ds4;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g4 + e;
+                float pr = __builtin_amdgcn_exp2f(fmaf(sc[r], a.scale_log2, -lv[e]));
+                if constexpr (decltype(masked)::value)
+                  if (kofs + col > q0 + rq + e) pr = 0.f;   // key after the query
+                p4[e] = static_cast<bf16>(pr);
+                ds4[e] = static_cast<bf16>(pr * (dp[r] - dv[e]));
+              }
+              *reinterpret_cast<bf16x4*>(xp + 2 * rq) = p4;
+              *reinterpret_cast<bf16x4*>(xs + 2 * rq) = ds4;
+            }
+          };
+          // Only own tiles whose (key group, query half) square crosses the
+          // diagonal hold keys after a query; the rest skip the mask (uniform branch).
+          if (own && kofs + 31 > q0 + 32 * qh) softmax(std::true_type{});
+          else softmax(std::false_type{});
+        }
+      }
+      step_end(st);
+    }
+    return;
+  }
+  // Waves 4-7: dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS over all D dims of the key group,
+  // for tile st - 1 (dOᵀ, Qᵀ by transpose reads; P, dS from the exchange).
+  f32x16 adv[D / 32], adk[D / 32];
+#pragma unroll
+  for (int dc = 0; dc < D / 32; ++dc)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) adv[dc][r] = adk[dc][r] = 0.f;
+  for (int st = 0; st <= t_all; ++st) {
+    step_begin(st);
+    const int i = st - 1;
+    if (active && i >= 0 && !(i >= t_past && kofs > tile_q0(i) + kBwdQTile - 1)) {   // (all P = 0 otherwise)
+      const int buf = i & 1;
+      const char* qt = tiles[buf];
+      const char* dt = tiles[buf] + L::kTile;
+      const char* xp = xch[buf][0] + xrow;
+      const char* xs = xch[buf][1] + xrow;
 #pragma unroll
       for (int g = 0; g < kBwdQTile / 16; ++g) {
         const int q16 = 16 * g + 4 * half;
         const bf16x4 pa = *reinterpret_cast<const bf16x4*>(xp + 2 * q16);
         const bf16x4 pb = *reinterpret_cast<const bf16x4*>(xp + 2 * (q16 + 8));
-        const bf16x4 sa = *reinterpret_cast<const bf16x4*>(xp + 4 * kX + 2 * q16);
-        const bf16x4 sb = *reinterpret_cast<const bf16x4*>(xp + 4 * kX + 2 * (q16 + 8));
+        const bf16x4 sa = *reinterpret_cast<const bf16x4*>(xs + 2 * q16);
+        const bf16x4 sb = *reinterpret_cast<const bf16x4*>(xs + 2 * (q16 + 8));
         const bf16x8 pp = bf16x8{pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
         const bf16x8 dsp = bf16x8{sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
-        const int roff = 16 * g * L::kRow + tr_lane + 2 * kDH * wh;
+        const int roff = 16 * g * L::kRow + tr_lane;
 #pragma unroll
-        for (int dc = 0; dc < kDH / 32; ++dc) {
+        for (int dc = 0; dc < D / 32; ++dc) {
           const bf16x8 dot = tr_operand<L::kRow>(dt + roff + 64 * dc);
           adv[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot, pp, adv[dc], 0, 0, 0);
           const bf16x8 qtr = tr_operand<L::kRow>(qt + roff + 64 * dc);
@@ -336,17 +378,16 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
         }
       }
     }
-    if (i + 1 < t_all) commit(buf ^ 1);
-    __syncthreads();
+    step_end(st);
   }
   if (!active) return;
-  // dKᵀ / dVᵀ rows are dims kDH wh + 32 dc + 8 g4 + 4 half + 0..3 of this lane's key.
+  // dKᵀ / dVᵀ rows are dims 32 dc + 8 g4 + 4 half + 0..3 of this lane's key.
   const int64_t base = (key0 + col) * row_el + hd;
 #pragma unroll
-  for (int dc = 0; dc < kDH / 32; ++dc)
+  for (int dc = 0; dc < D / 32; ++dc)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      const int d0 = kDH * wh + 32 * dc + 8 * g4 + 4 * half;
+      const int d0 = 32 * dc + 8 * g4 + 4 * half;
       bf16x4 kv4, vv4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
