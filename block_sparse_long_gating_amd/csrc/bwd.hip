@@ -147,10 +147,10 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
 // dK, dV
 // ---------------------------------------------------------------------------
 
-// Eight waves over 128 keys: wave w computes S and dP for key group kg = w % 4
-// (32 keys, K and V in registers) and query half w / 4 of each 64-query tile,
-// hands P and dS to the workgroup through LDS, then accumulates dKᵀ and dVᵀ
-// for key group kg and dims half w / 4 over the whole tile.
+// Eight waves over 128 keys in a two-stage pipeline over the 64-query tiles:
+// wave w < 4 computes S, dP, P and dS of tile i for key group w (32 keys, K
+// and V in registers) and hands P and dS over through LDS; wave w + 4, on the
+// same SIMD, meanwhile accumulates dKᵀ and dVᵀ of key group w over tile i - 1.
 template <int D>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
   using L = BwdLay<D>;
@@ -359,24 +359,42 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
       const char* dt = tiles[buf] + L::kTile;
       const char* xp = xch[buf][0] + xrow;
       const char* xs = xch[buf][1] + xrow;
-#pragma unroll
-      for (int g = 0; g < kBwdQTile / 16; ++g) {
+      // Operands of one 16-query group; the next group's are read before the
+      // current group's products are issued.
+      struct Ops {
+        bf16x8 dot[D / 32], qtr[D / 32], pp, dsp;
+      };
+      auto read_ops = [&](int g, Ops& o) {
         const int q16 = 16 * g + 4 * half;
         const bf16x4 pa = *reinterpret_cast<const bf16x4*>(xp + 2 * q16);
         const bf16x4 pb = *reinterpret_cast<const bf16x4*>(xp + 2 * (q16 + 8));
         const bf16x4 sa = *reinterpret_cast<const bf16x4*>(xs + 2 * q16);
         const bf16x4 sb = *reinterpret_cast<const bf16x4*>(xs + 2 * (q16 + 8));
-        const bf16x8 pp = bf16x8{pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
-        const bf16x8 dsp = bf16x8{sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+        o.pp = bf16x8{pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
+        o.dsp = bf16x8{sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
         const int roff = 16 * g * L::kRow + tr_lane;
 #pragma unroll
         for (int dc = 0; dc < D / 32; ++dc) {
-          const bf16x8 dot = tr_operand<L::kRow>(dt + roff + 64 * dc);
-          adv[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot, pp, adv[dc], 0, 0, 0);
-          const bf16x8 qtr = tr_operand<L::kRow>(qt + roff + 64 * dc);
-          adk[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qtr, dsp, adk[dc], 0, 0, 0);
+          o.dot[dc] = tr_operand<L::kRow>(dt + roff + 64 * dc);
+          o.qtr[dc] = tr_operand<L::kRow>(qt + roff + 64 * dc);
         }
-      }
+      };
+      auto products = [&](const Ops& o) {
+#pragma unroll
+        for (int dc = 0; dc < D / 32; ++dc) {
+          adv[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.dot[dc], o.pp, adv[dc], 0, 0, 0);
+          adk[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.qtr[dc], o.dsp, adk[dc], 0, 0, 0);
+        }
+      };
+      Ops o0, o1;
+      read_ops(0, o0);
+      read_ops(1, o1);
+      products(o0);
+      read_ops(2, o0);
+      products(o1);
+      read_ops(3, o1);
+      products(o0);
+      products(o1);
     }
     step_end(st);
   }
