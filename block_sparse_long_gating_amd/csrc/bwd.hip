@@ -588,11 +588,10 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
           }
         }
       }
+      // Buffer buf ^ 1 was last read by tile i - 1, which every wave finished
+      // before the previous barrier: one barrier per tile suffices.
+      if (i + 1 < ntiles) commit(buf ^ 1);
       __syncthreads();
-      if (i + 1 < ntiles) {
-        commit(buf ^ 1);
-        __syncthreads();
-      }
     }
     // dQᵀ rows are dims 32 dc + 8 g4 + 4 half + 0..3 of this lane's query.
     if (!kOwn) {
