@@ -555,36 +555,41 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
       if (i + 1 < ntiles) fetch(i + 1);
       const char* kt = tiles[buf];
       const char* vt = tiles[buf] + L::kTile;
+      // Past items test only whether the wave holds queries (once per tile),
+      // which leaves both halves in one block for the scheduler; own items
+      // also skip the halves that lie wholly after the wave's queries.
+      if (kOwn || wlast >= 0) {
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        const int64_t kbase = kb0 + kBwdKTile * i + 32 * kh;
-        if (kbase > wlast) continue;
-        const f32x16 s = rows_by_regs<D>(kt + kh * 32 * L::kRow + row_lane, qr);
-        const f32x16 dp = rows_by_regs<D>(vt + kh * 32 * L::kRow + row_lane, dr);
-        f32x16 ds;
-        auto softmax = [&](auto masked) {
-          const int rel = masked ? static_cast<int>(t - kbase) - 4 * half : 0;   // |t - kbase| < B
+        for (int kh = 0; kh < 2; ++kh) {
+          const int64_t kbase = kb0 + kBwdKTile * i + 32 * kh;
+          if (kOwn && kbase > wlast) continue;
+          const f32x16 s = rows_by_regs<D>(kt + kh * 32 * L::kRow + row_lane, qr);
+          const f32x16 dp = rows_by_regs<D>(vt + kh * 32 * L::kRow + row_lane, dr);
+          f32x16 ds;
+          auto softmax = [&](auto masked) {
+            const int rel = masked ? static_cast<int>(t - kbase) - 4 * half : 0;   // |t - kbase| < B
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float pr = __builtin_amdgcn_exp2f(fmaf(s[r], a.scale_log2, -lse2));
-            if constexpr (decltype(masked)::value)
-              if (8 * (r >> 2) + (r & 3) > rel) pr = 0.f;   // key after the query
-            ds[r] = pr * (dp[r] - del);
-          }
-        };
-        // Own items: only a key half that crosses the diagonal of the wave's
-        // queries holds keys after a query (uniform branch).
-        if (kOwn && kbase + 31 > t0 + 32 * w) softmax(std::true_type{});
-        else softmax(std::false_type{});
-        bf16x8 dsp[2];
-        pack16(ds, dsp);
+            for (int r = 0; r < 16; ++r) {
+              float pr = __builtin_amdgcn_exp2f(fmaf(s[r], a.scale_log2, -lse2));
+              if constexpr (decltype(masked)::value)
+                if (8 * (r >> 2) + (r & 3) > rel) pr = 0.f;   // key after the query
+              ds[r] = pr * (dp[r] - del);
+            }
+          };
+          // Own items: only a key half that crosses the diagonal of the wave's
+          // queries holds keys after a query (uniform branch).
+          if (kOwn && kbase + 31 > t0 + 32 * w) softmax(std::true_type{});
+          else softmax(std::false_type{});
+          bf16x8 dsp[2];
+          pack16(ds, dsp);
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const int roff = (kh * 32 + 16 * g) * L::kRow + tr_lane;
+          for (int g = 0; g < 2; ++g) {
+            const int roff = (kh * 32 + 16 * g) * L::kRow + tr_lane;
 #pragma unroll
-          for (int dc = 0; dc < D / 32; ++dc) {
-            const bf16x8 ktr = tr_operand<L::kRow>(kt + roff + 64 * dc);
-            acc[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktr, dsp[g], acc[dc], 0, 0, 0);
+            for (int dc = 0; dc < D / 32; ++dc) {
+              const bf16x8 ktr = tr_operand<L::kRow>(kt + roff + 64 * dc);
+              acc[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktr, dsp[g], acc[dc], 0, 0, 0);
+            }
           }
         }
       }
