@@ -283,6 +283,7 @@ BACKWARD = [  # (N, H, D, B, topk, seed)
     (1024, 1, 128, 128, 16, 5),      # top_k > n: full causal attention
     (1536, 2, 64, 192, 4, 6),        # B not a multiple of 128 or 256
     (4096, 1, 128, 256, 5, 7),
+    (1920, 2, 128, 320, 3, 8),       # D = 128, last 128-key chunk half empty, own tiles of 256 + 64 queries
 ]
 # Gradients are compared with the fp64 oracle (same selection) relative to the
 # largest |gradient| of each tensor (max-norm) and in relative L2: the GPU
