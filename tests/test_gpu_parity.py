@@ -44,6 +44,8 @@ SMALL = [
     (640, 1, 64, 64, 5, "fp32", 13),
     (4096, 1, 128, 64, 32, "bf16", 14),
     (1024, 40, 64, 128, 4, "bf16", 15),      # many heads, not a power of two
+    (1920, 2, 128, 320, 3, "bf16", 16),      # own tiles of 256 + 64 queries, 5 key tiles per block
+    (1536, 2, 128, 192, 4, "bf16", 17),      # own tiles of 192 queries, 3 key tiles per block
 ]
 
 
