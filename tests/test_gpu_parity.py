@@ -390,22 +390,26 @@ def test_pooling_variants(moba, case):
         assert not np.array_equal(gsel, moba.gate_topk(qd, kd, B, topk).cpu().numpy())
 
 
-def test_backward_pooled(moba):
+@pytest.mark.parametrize("pooling", ["max", "weighted"])
+def test_backward_pooled(moba, pooling):
     """The backward pass recomputes the selection with the same pooling."""
     from oracle import moba_backward_ref
     N, H, D, B, topk = 1024, 2, 128, 128, 3
     q, k, v = synth.make_qkv(N, H, D, seed=[510, 0], dtype="bf16")
     do = synth.make_grad(N, H, D, seed=[510, 1])
+    w = np.random.default_rng([510, 2]).uniform(0.0, 1.0, (H, N)).astype(np.float32) \
+        if pooling == "weighted" else None
     qd, kd, vd, dod = (to_device(x, "bf16") for x in (q, k, v, do))
-    out, lse = moba.prefill_pooled(qd, kd, vd, B, topk, "max")
-    dq, dk, dv = moba.prefill_backward(qd, kd, vd, out, lse, dod, B, topk, pooling="max")
-    sel = moba.gate_topk_pooled(qd, kd, B, topk, "max")
+    wd = torch.from_numpy(w).cuda() if w is not None else None
+    out, lse = moba.prefill_pooled(qd, kd, vd, B, topk, pooling, wd)
+    dq, dk, dv = moba.prefill_backward(qd, kd, vd, out, lse, dod, B, topk, pooling=pooling, weights=wd)
+    sel = moba.gate_topk_pooled(qd, kd, B, topk, pooling, wd)
     torch.cuda.synchronize()
     rq, rk, rv, _ = moba_backward_ref(q, k, v, do, B, topk, sel=sel.cpu().numpy())
     for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
         g = got.float().cpu().numpy().astype(np.float64)
         rel = float(np.linalg.norm(g - ref) / np.linalg.norm(ref))
-        log(f"  backward max-pooled {name}: rel L2 {rel:.3e}")
+        log(f"  backward {pooling}-pooled {name}: rel L2 {rel:.3e}")
         assert rel <= GRAD_L2_TOL and float(np.max(np.abs(g - ref))) <= GRAD_REL_TOL * float(np.max(np.abs(ref)))
 
 
