@@ -26,6 +26,12 @@ generation loop keeps them): once gated with the workload's top-k and once
 with top-k above the block count (full attention over the whole cache).
 Decode reads 4*D bytes of keys and values per attended key and head, so it is
 priced against HBM.
+
+A ``configs`` object times the other workloads of the same family (the long
+contexts n128k and m1, the one-head c32k and the fp32 tiny case): whole-call
+time, effective TFLOP/s and % of peak, the past-block kernel's launch time, and
+for the long ones the oracle on a seeded sample of query rows with a labelled
+full-size extrapolation.
 """
 
 from __future__ import annotations
@@ -228,6 +234,49 @@ def varlen_bench(moba, w, qd, kd, vd, steps: int, nseq: int = 8):
             "effective_tflops": flops / (ms * 1e-3) / 1e12}
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_flops(w, rows: np.ndarray) -> float:
+    """FLOPs the oracle itself spends on ``rows`` (all heads) with its
+    per-block evaluation: every chosen block's B logits twice (row maxima,
+    then exponentials) and its B values once, 6 D B per chosen block and row,
+    plus the gate's scores against all n block means, 2 D n per row."""
+    j = rows // w.block_size
+    kept = np.minimum(w.topk, j + 1)
+    n = w.N // w.block_size
+    return float(w.H * np.sum(6.0 * w.D * w.block_size * kept + 2.0 * w.D * n))
+
+
+def sample_parity(w, q, k, rows, out, lse, sel, gpu_out_rows, gpu_lse_rows, gpu_sel_rows):
+    """GPU results against the oracle's on sampled rows: outputs compared on
+    the (row, head) pairs whose selection equals the oracle's; differing
+    selections checked for the near-tie exemption (both denominators)."""
+    from tests.parity import compare_selection
+    same = np.all(gpu_sel_rows == sel, axis=2)                   # [H, R]
+    d_out = np.max(np.abs(gpu_out_rows.astype(np.float64) - out), axis=2).T   # [H, R]
+    d_lse = np.abs(gpu_lse_rows - lse)                           # [H, R]
+    cmp = compare_selection(gpu_sel_rows, sel, q, k, w.block_size, w.topk, rows=rows)
+    return {
+        "rows": int(rows.shape[0]),
+        "pairs_same_selection": int(same.sum()),
+        "pairs_other_selection": int((~same).sum()),
+        "other_selection_near_tie": cmp["exempt"],
+        "other_selection_near_tie_rowmax": cmp["exempt_rowmax"],
+        "other_selection_not_tie": len(cmp["bad"]),
+        "max_abs_out": float(np.max(d_out[same])) if same.any() else None,
+        "max_abs_lse": float(np.max(d_lse[same])) if same.any() else None,
+    }
+
+
 def cpu_baseline(w, q, k, v, gpu_out, gpu_lse, gpu_sel, target_s: float):
     """The fp64 oracle as it stands, on a seeded sample of query rows; the
     GPU outputs are compared with it on the (row, head) pairs whose block
@@ -254,6 +303,7 @@ def cpu_baseline(w, q, k, v, gpu_out, gpu_lse, gpu_sel, target_s: float):
             break
         R = min(w.N, int(R * max(2.0, target_s / max(dt, 1e-3))))
     flops = 4.0 * w.D * w.H * row_pairs(rows, w.block_size, w.topk)
+    full = R >= w.N
     res = {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
@@ -262,21 +312,93 @@ def cpu_baseline(w, q, k, v, gpu_out, gpu_lse, gpu_sel, target_s: float):
         "sample": f"{R} seeded query rows x {w.H} heads of the {w.name} workload "
                   f"(gate over all blocks + fp64 softmax over the attended keys); {dt:.2f} s; "
                   f"{cores} cores visible, BLAS threads {threads}",
+        "cpu_model": cpu_model(),
+        "cores_visible": cores,
         "seconds": dt,
         "rows": int(R),
+        "rows_per_s": R * w.H / dt,
+        "effective_gflop": flops / 1e9,
+        "oracle_gflop": oracle_flops(w, rows) / 1e9,
+        "oracle_gflops_rate": oracle_flops(w, rows) / dt / 1e9,
+        "full_call_s": dt if full else None,
+        "full_call_s_extrapolated": None if full else dt * w.N / R,
     }
-    got = gpu_out[rows].astype(np.float64)                       # [R, H, D]
-    same = np.all(gpu_sel[:, rows, :] == sel, axis=2)            # [H, R]
-    d_out = np.max(np.abs(got - out), axis=2).T                  # [H, R]
-    d_lse = np.abs(gpu_lse[:, rows] - lse)                       # [H, R]
-    res_parity = {
-        "rows": int(R),
-        "pairs_same_selection": int(same.sum()),
-        "pairs_other_selection": int((~same).sum()),
-        "max_abs_out": float(np.max(d_out[same])) if same.any() else None,
-        "max_abs_lse": float(np.max(d_lse[same])) if same.any() else None,
-    }
+    res_parity = sample_parity(w, q, k, rows, out, lse, sel, gpu_out[rows], gpu_lse[:, rows], gpu_sel[:, rows, :])
     return res, res_parity
+
+
+def configs_bench(moba, names, steps: int, cpu_rows: int, with_cpu: bool):
+    """The whole prefill call on the other workloads (their own inputs),
+    with the past-block kernel's launch time, and the oracle on a seeded row
+    sample of the long ones (GPU parity on the same rows)."""
+    import torch
+
+    from block_sparse_long_gating_amd import synth
+    res = {}
+    for name in names:
+        w, q, k, v = synth.make_workload(name)
+        dev = torch.device("cuda:0")
+        if w.dtype == "bf16":
+            qd, kd, vd = (torch.from_numpy(synth.bf16_bits(x)).view(torch.bfloat16).to(dev) for x in (q, k, v))
+        else:
+            qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+        out = torch.empty_like(qd)
+        lse = torch.empty((w.H, w.N), dtype=torch.float32, device=dev)
+        nsteps = steps if effective_pairs(w.N, w.block_size, w.topk) * w.H < 10 ** 10 else max(3, steps // 4)
+        for _ in range(3):
+            moba.prefill(qd, kd, vd, w.block_size, w.topk, out=out, lse=lse)
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(nsteps):
+            moba.prefill(qd, kd, vd, w.block_size, w.topk, out=out, lse=lse)
+        stop.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(stop) / nsteps
+        flops = 4.0 * w.D * w.H * effective_pairs(w.N, w.block_size, w.topk)
+        r = {"N": w.N, "H": w.H, "D": w.D, "block_size": w.block_size, "top_k": w.topk, "dtype": w.dtype,
+             "steps": nsteps, "ms_per_step": ms, "effective_gflop": flops / 1e9,
+             "effective_tflops": flops / (ms * 1e-3) / 1e12,
+             "pct_peak": 100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        if w.dtype == "bf16":
+            events = [moba.StageEvents(stages=("attn_past",)) for _ in range(nsteps)]
+            for i in range(nsteps):
+                moba.prefill(qd, kd, vd, w.block_size, w.topk, out=out, lse=lse, events=events[i])
+            torch.cuda.synchronize()
+            for e in events:
+                e.accumulate()
+            past_ms = sum(e.totals["attn_past"] for e in events) / nsteps
+            for e in events:
+                e.close()
+            pf = 4.0 * w.D * w.H * past_pairs(w.N, w.block_size, w.topk)
+            r["past_kernel"] = {"launch_us": 1e3 * past_ms, "gflop": pf / 1e9,
+                                "tflops": pf / (past_ms * 1e-3) / 1e12 if past_ms > 0 else None,
+                                "frac": pf / (past_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS if past_ms > 0 else None}
+        print(f"[bench] {name}: {ms:.3f} ms/step, {r['effective_tflops']:.1f} effective TFLOP/s "
+              f"({r['pct_peak']:.1f}% of peak)", file=sys.stderr, flush=True)
+        if with_cpu and name in ("n128k", "m1"):
+            from oracle import moba_ref
+            rows = synth.sample_rows(w.N, cpu_rows, synth.SAMPLE_SEED[name])
+            t0 = time.perf_counter()
+            o_out, o_lse, o_sel = moba_ref(q, k, v, w.block_size, w.topk, rows=rows)
+            dt = time.perf_counter() - t0
+            of = oracle_flops(w, rows)
+            ef = 4.0 * w.D * w.H * row_pairs(rows, w.block_size, w.topk)
+            r["cpu_oracle"] = {
+                "kind": "oracle", "rows": int(rows.shape[0]), "heads": w.H, "seconds": dt,
+                "rows_per_s": rows.shape[0] * w.H / dt, "effective_tflops": ef / dt / 1e12,
+                "oracle_gflop": of / 1e9, "cpu_model": cpu_model(),
+                "full_call_s_extrapolated": dt * w.N / rows.shape[0],
+                "note": "sampled rows; the full-size time is extrapolated linearly in the row count",
+            }
+            sel = moba.gate_topk(qd, kd, w.block_size, w.topk).cpu().numpy()[:, rows, :]
+            r["parity_sample"] = sample_parity(w, q, k, rows, o_out, o_lse, o_sel,
+                                               out.float().cpu().numpy()[rows], lse.cpu().numpy()[:, rows], sel)
+        res[name] = r
+        del qd, kd, vd, out, lse, q, k, v
+        torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -299,6 +421,12 @@ def main():
                     help="also time the backward pass on the same workload")
     ap.add_argument("--decode", choices=("on", "off"), default="on",
                     help="also time the decode step on the same cache")
+    ap.add_argument("--configs", default="n128k,m1,c32k,tiny",
+                    help="other workloads to time after the headline one (comma list; 'none' for none)")
+    ap.add_argument("--config-cpu-rows", type=int, default=1024,
+                    help="oracle rows sampled per long workload for its CPU time and parity")
+    ap.add_argument("--per-call-ms", type=int, default=0,
+                    help="before the warm-up, time this many single calls with HIP events (prints them)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run plain device copies of this size (HBM counter calibration)")
     args = ap.parse_args()
@@ -330,6 +458,18 @@ def main():
     out = torch.empty_like(qd)
     lse = torch.empty((w.H, w.N), dtype=torch.float32, device=dev)
     print(f"[bench] workload {w.name}: {w.description}", file=sys.stderr, flush=True)
+
+    if args.per_call_ms > 0:
+        # Per-call device times from the first call on (warm-up behaviour).
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.per_call_ms)]
+        for a, b in evs:
+            a.record()
+            moba.prefill(qd, kd, vd, w.block_size, w.topk, out=out, lse=lse)
+            b.record()
+        torch.cuda.synchronize()
+        times = [a.elapsed_time(b) for a, b in evs]
+        print("[bench] per-call ms: " + " ".join(f"{t:.3f}" for t in times), file=sys.stderr, flush=True)
 
     for _ in range(args.warmup):
         moba.prefill(qd, kd, vd, w.block_size, w.topk, out=out, lse=lse)
@@ -465,10 +605,16 @@ def main():
         got_lse = lse.cpu().numpy()
         got_sel = moba.gate_topk(qd, kd, w.block_size, w.topk).cpu().numpy()
         cb, parity = cpu_baseline(w, q, k, v, got_out, got_lse, got_sel, args.cpu_seconds)
-        result["cpu_baseline"] = {kk: cb[kk] for kk in ("value", "unit", "cores", "kind", "sample")}
+        result["cpu_baseline"] = cb
         result["parity_sample"] = parity
     else:
         result["cpu_baseline"] = None
+
+    names = [x for x in args.configs.split(",") if x and x != "none" and x != w.name]
+    if names:
+        del qd, kd, vd, out, lse
+        torch.cuda.empty_cache()
+        result["configs"] = configs_bench(moba, names, args.steps, args.config_cpu_rows, args.cpu_baseline == "on")
     print(json.dumps(result), flush=True)
 
 

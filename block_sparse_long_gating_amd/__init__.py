@@ -15,7 +15,7 @@ import ctypes
 import os
 
 __all__ = ["prefill", "gate_topk", "block_mean_keys", "MobaError", "library_path", "load_library",
-           "StageEvents", "STAGES", "STATUS", "MAX_TOPK", "MAX_BLOCKS"]
+           "StageEvents", "STAGES", "STATUS", "MAX_TOPK", "MAX_BLOCKS", "debug_poison_workspace"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmoba.so")
@@ -48,6 +48,7 @@ _SIGNATURES = {
     "moba_gate_topk_varlen": [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P],
     "moba_prefill_fwd_varlen": [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P],
     "moba_prefill_bwd_varlen": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P],
+    "moba_debug_poison_workspace": [ctypes.c_int],
     "moba_status_string": [ctypes.c_int],
     "moba_last_hip_error": [],
 }
@@ -86,6 +87,13 @@ def load_library():
         lib.moba_topk_for_sparsity.restype = ctypes.c_int32
         _lib = lib
     return _lib
+
+
+def debug_poison_workspace(on: bool) -> bool:
+    """Switch the library's workspace poisoning on or off (every later call
+    fills its workspace with 0xFF bytes before its first stage); returns the
+    previous setting."""
+    return bool(load_library().moba_debug_poison_workspace(1 if on else 0))
 
 
 def _check(status: int, where: str):

@@ -12,6 +12,8 @@
 //      start(list) + prefix(tile) + rank-in-tile; the position is also kept per
 //      query so the merge can find its partial outputs again.
 // Only integer arithmetic in fixed orders: the lists are deterministic.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -139,6 +141,24 @@ hipError_t launch_csr(const Problem& p, const Workspace& ws, const int32_t* sel,
   if (p.lmax > 0)
     scatter_kernel<<<static_cast<unsigned>((threads + 255) / 256), 256, 0, stream>>>(
         sel, ws.rk, ws.cnt, ws.offs, ws.qidx, ws.inv, p.N, p.H, p.B, p.n, p.topk, p.lmax, p.ntiles, p.blo);
+  return hipGetLastError();
+}
+
+namespace {
+
+__global__ __launch_bounds__(256) void fill_kernel(uint4* __restrict__ p, size_t n16, uint32_t value) {
+  const uint4 x = make_uint4(value, value, value, value);
+  for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n16; i += static_cast<size_t>(gridDim.x) * 256)
+    p[i] = x;
+}
+
+}  // namespace
+
+hipError_t launch_fill(void* p, size_t bytes, uint32_t value, hipStream_t stream) {
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  const size_t blocks = std::min<size_t>((n16 + 255) / 256, 4096);
+  fill_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(static_cast<uint4*>(p), n16, value);
   return hipGetLastError();
 }
 

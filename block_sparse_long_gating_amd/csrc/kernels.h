@@ -39,6 +39,9 @@ struct SeqStarts {
 };
 hipError_t launch_seq_lo(const SeqStarts& st, int32_t* blo, int n, hipStream_t stream);
 
+// Fills `bytes` (a multiple of 16) at the 16-byte aligned `p` with copies of `value`.
+hipError_t launch_fill(void* p, size_t bytes, uint32_t value, hipStream_t stream);
+
 // Block pooling modes (MOBA_POOL_* in moba.h).
 constexpr int kPoolMean = 0, kPoolMax = 1, kPoolWeighted = 2;
 // Block keys (and their 3-way bf16 split when `pieces` is not null). `weights`

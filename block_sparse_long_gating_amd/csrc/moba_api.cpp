@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -14,6 +15,7 @@
 namespace {
 
 thread_local int g_last_hip_error = 0;
+std::atomic<int> g_poison_workspace{0};   // moba_debug_poison_workspace
 
 constexpr int kMaxDevices = 64;
 
@@ -105,7 +107,10 @@ moba::Problem make_problem(int64_t N, int32_t H, int32_t D, int32_t B, int32_t t
   p.D = D;
   p.B = B;
   p.n = static_cast<int>(N / B);
-  p.topk = topk;
+  // A query of block j keeps min(topk, j + 1) <= n blocks: a larger topk
+  // selects the same blocks as topk = n, so the internal selection rows are n
+  // wide at most (moba_gate_topk still fills the caller's topk-wide rows).
+  p.topk = static_cast<int>(std::min<int64_t>(topk, p.n));
   p.lmax = static_cast<int>(std::min<int64_t>(topk - 1, p.n - 1));
   p.ntiles = static_cast<int>((N + moba::kQTile - 1) / moba::kQTile);
   int64_t pairs_per_head = 0;  // sum over blocks j of B * min(topk - 1, j)
@@ -201,6 +206,14 @@ int alloc_ws(DeviceState* st, size_t bytes, hipStream_t stream, char** out) {
   }
   if (e != hipSuccess) return hip_fail(e);
   *out = static_cast<char*>(p);
+  if (g_poison_workspace.load(std::memory_order_relaxed) != 0) {
+    // Layout rounds every piece to 256 bytes, so the total is a multiple of 16.
+    e = moba::launch_fill(p, bytes, 0xFFFFFFFFu, stream);
+    if (e != hipSuccess) {
+      (void)hipFreeAsync(p, stream);
+      return hip_fail(e);
+    }
+  }
   return MOBA_OK;
 }
 
@@ -262,6 +275,7 @@ int parse_packed(const int64_t* cu, int32_t num_seqs, int32_t B, int32_t topk, P
 // The problem of packed sequences: list sizes from the sequences' own blocks.
 void apply_packed(const Packed& pk, moba::Problem* p) {
   p->p_off = pk.pairs_per_head * p->H;
+  p->topk = std::max(1, std::min(p->topk, pk.max_blocks));   // the longest sequence bounds the kept blocks
   p->lmax = std::max(0, std::min(p->topk - 1, pk.max_blocks - 1));
   p->max_items = p->p_off / moba::kAttnTile + static_cast<int64_t>(p->H) * p->n;
 }
@@ -291,6 +305,7 @@ int gate_impl(const void* q, const void* k, int32_t* sel, int64_t N, int32_t H, 
   if ((s = current_device(&st)) != MOBA_OK) return s;
   moba::Problem p = make_problem(N, H, D, B, topk, is_f32);
   if (pk != nullptr) apply_packed(*pk, &p);
+  p.topk = topk;   // the caller's rows are topk wide (entries past j + 1 are -1)
   const WsPlan w = plan(p, false, false, pk != nullptr);
   char* base = nullptr;
   if ((s = alloc_ws(st, w.total, stream, &base)) != MOBA_OK) return s;
@@ -634,5 +649,7 @@ const char* moba_status_string(int status) {
 }
 
 int moba_last_hip_error(void) { return g_last_hip_error; }
+
+int moba_debug_poison_workspace(int on) { return g_poison_workspace.exchange(on != 0 ? 1 : 0); }
 
 }  // extern "C"

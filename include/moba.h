@@ -260,6 +260,18 @@ int moba_decode_fwd(const void* q, const void* k, const void* v, const float* kb
                     void* out, float* lse, int32_t* sel, int64_t N, int32_t H, int32_t D,
                     int32_t block_size, int32_t topk, hipStream_t stream);
 
+/*
+ * Debug aid for the workspace (the lists, partial outputs and counters the
+ * stages hand to each other, e.g. the regrouped query lists of the 智东西
+ * report, section 二, implementation step 2). With `on` non-zero, every later
+ * call that takes workspace memory first fills all of it with 0xFF bytes (NaN
+ * in fp32 and bf16, -1 in int32) by a fill kernel on its stream, so that a
+ * stage reading workspace it did not write first shows up as non-finite or
+ * different output. Process-wide switch, off by default; it changes no
+ * result of a correct call. Returns the previous setting.
+ */
+int moba_debug_poison_workspace(int on);
+
 /* Static, NUL-terminated name of a status code ("MOBA_OK", ...). */
 const char* moba_status_string(int status);
 

@@ -123,6 +123,28 @@ def pin_bruteforce_tiny(m):
         assert np.allclose(lse, blse, rtol=0, atol=1e-12), f"lse differs from masked logsumexp at {N, B, topk}"
 
 
+def pin_chunked_loops(m):
+    """The oracle's chunk loops against the brute-force routes, with chunks so
+    small that every call runs several of them and a ragged last one: the gate
+    over row chunks of 7 (select_blocks), and the dense attention over row
+    chunks of 5 inside each query block (moba_ref's max_rows_chunk)."""
+    for N, H, D, B, topk, seed in TINY_CASES:
+        q, k, v = _rand(N, H, D, seed)
+        bsel = brute_selection(q, k, B, topk)
+        sel, _ = m.select_blocks(q, k, B, topk, chunk=7)
+        assert np.array_equal(sel, bsel), f"chunked selection differs from exhaustive search at {N, B, topk}"
+        rows = np.arange(3, N, 2)          # a row subset: chunk boundaries fall between chosen rows
+        sel_r, _ = m.select_blocks(q, k, B, topk, rows=rows, chunk=7)
+        assert np.array_equal(sel_r, bsel[:, rows]), f"chunked row-subset selection differs at {N, B, topk}"
+        bout, blse = brute_attention(q, k, v, B, bsel)
+        out, lse, _ = m.moba_ref(q, k, v, B, topk, method="dense", max_rows_chunk=5)
+        assert np.allclose(out, bout, rtol=0, atol=1e-12), f"chunked dense output differs at {N, B, topk}"
+        assert np.allclose(lse, blse, rtol=0, atol=1e-12), f"chunked dense lse differs at {N, B, topk}"
+        out_r, lse_r, _ = m.moba_ref(q, k, v, B, topk, rows=rows, method="dense", max_rows_chunk=3)
+        assert np.allclose(out_r, bout[rows], rtol=0, atol=1e-12), f"chunked row-subset output differs at {N, B}"
+        assert np.allclose(lse_r, blse[:, rows], rtol=0, atol=1e-12), f"chunked row-subset lse differs at {N, B}"
+
+
 def pin_full_causal(m):
     """top_k >= n selects every past block: plain causal attention."""
     for N, H, D, B, seed in [(64, 2, 8, 8, 21), (96, 1, 16, 16, 22)]:
@@ -649,7 +671,7 @@ def pin_varlen_one_sequence_and_order(m):
 
 
 ALL_PINS = [
-    pin_bruteforce_tiny, pin_full_causal, pin_block_diagonal, pin_first_token, pin_constant_v,
+    pin_bruteforce_tiny, pin_chunked_loops, pin_full_causal, pin_block_diagonal, pin_first_token, pin_constant_v,
     pin_zero_query, pin_invariants, pin_pages_worked_example, pin_pages_sparsity_table,
     pin_granularity, pin_closed_form_pairs, pin_lse_merge, pin_pooling_linearity,
     pin_gate_rounding, pin_row_mode_matches, pin_decode_full_attention, pin_decode_own_block,

@@ -60,6 +60,15 @@ def test_status_strings(lib):
     assert lib.moba_last_hip_error() == 0
 
 
+def test_poison_switch_is_host_state(lib):
+    """The workspace-poisoning switch only flips host state and returns the
+    previous setting (no GPU needed)."""
+    assert lib.moba_debug_poison_workspace(1) == 0
+    assert lib.moba_debug_poison_workspace(7) == 1
+    assert lib.moba_debug_poison_workspace(0) == 1
+    assert lib.moba_debug_poison_workspace(0) == 0
+
+
 # Fake, never dereferenced, 16-byte aligned addresses: every call below must be
 # rejected by the host-side checks before any HIP call.
 A = 0x10000

@@ -28,6 +28,8 @@ def test_package_exports():
 MUTATIONS = {
     "no_forced_current_block": ("sorted(order[i, :topk - 1].tolist() + [int(j)])",
                                 "sorted(order[i, :topk].tolist())"),
+    "gate_chunk_offset_dropped": ("sel[h, c0 + i, :len(row)] = row", "sel[h, i, :len(row)] = row"),
+    "dense_chunk_drops_last_row": ("idx = in_j[c0:c0 + max_rows_chunk]", "idx = in_j[c0:c0 + max_rows_chunk - 1]"),
     "causal_mask_off_by_one": ("chosen[:, key_block] & (key_pos[None, :] <= t[:, None])",
                                "chosen[:, key_block] & (key_pos[None, :] < t[:, None] + 2)"),
     "future_blocks_compete": ("neg[np.arange(n)[None, :] >= jj[:, None]] = np.inf",
