@@ -48,6 +48,7 @@ _SIGNATURES = {
     "moba_gate_topk_varlen": [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P],
     "moba_prefill_fwd_varlen": [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P],
     "moba_prefill_bwd_varlen": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P],
+    "moba_decode_fwd_noalloc": [_P, _P, _P, _P, _I32, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P],
     "moba_debug_poison_workspace": [ctypes.c_int],
     "moba_status_string": [ctypes.c_int],
     "moba_last_hip_error": [],
@@ -395,7 +396,7 @@ def prefill_backward(q, k, v, out, lse, dout, block_size: int, topk: int, dq=Non
     return tuple(grads)
 
 
-def decode(q_new, k, v, block_size: int, topk: int, kbar=None, out=None, lse=None, sel=None):
+def decode(q_new, k, v, block_size: int, topk: int, kbar=None, out=None, lse=None, sel=None, noalloc=False):
     """MoBA decode step (bf16) for the token at position N - 1 of the cache.
 
     ``q_new`` [H, D]; ``k``, ``v`` [N, H, D] (the token's own key and value are
@@ -403,7 +404,8 @@ def decode(q_new, k, v, block_size: int, topk: int, kbar=None, out=None, lse=Non
     complete blocks (nb >= (N - 1) // block_size), e.g. from
     :func:`block_mean_keys` over the complete prefix. Returns
     ``(out [H, D] bf16, lse [H] fp32)``; ``sel`` (int32 [H, topk]) receives
-    the kept blocks when given."""
+    the kept blocks when given. ``noalloc`` calls the allocation-free entry
+    point (workspace in the library's fixed per-GPU scratch array)."""
     import torch
     if k.dim() != 3 or k.dtype != torch.bfloat16 or not k.is_cuda:
         raise ValueError("k must be a bf16 [N, H, D] GPU tensor")
@@ -429,6 +431,8 @@ def decode(q_new, k, v, block_size: int, topk: int, kbar=None, out=None, lse=Non
         if sel.shape != (H, topk) or sel.dtype != torch.int32 or not sel.is_contiguous():
             raise ValueError("sel must be a contiguous int32 [H, topk] tensor")
         sp = sel.data_ptr()
-    _check(lib.moba_decode_fwd(q_new.data_ptr(), k.data_ptr(), v.data_ptr(), kb, nb, out.data_ptr(), lse.data_ptr(),
-                               sp, N, H, D, block_size, topk, _stream(k.device)), "moba_decode_fwd")
+    fn, name = (lib.moba_decode_fwd_noalloc, "moba_decode_fwd_noalloc") if noalloc else \
+        (lib.moba_decode_fwd, "moba_decode_fwd")
+    _check(fn(q_new.data_ptr(), k.data_ptr(), v.data_ptr(), kb, nb, out.data_ptr(), lse.data_ptr(),
+              sp, N, H, D, block_size, topk, _stream(k.device)), name)
     return out, lse

@@ -92,6 +92,15 @@ struct DecodeArgs {
   float scale_log2;     // log2(e) / sqrt(D)
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// Records `e` as the calling thread's last HIP error; returns MOBA_ERR_HIP.
+int fail_hip(hipError_t e);
+// moba_decode_fwd with its workspace in the caller's `ws` (ws_bytes long)
+// instead of the library's pool: argument checks, then every launch on
+// `stream`; MOBA_ERR_UNSUPPORTED when the call needs more than ws_bytes.
+// Returns a moba status.
+int decode_with_workspace(const void* q, const void* k, const void* v, const float* kbar, int32_t kbar_blocks,
+                          void* out, float* lse, int32_t* sel, int64_t N, int32_t H, int32_t D, int32_t block_size,
+                          int32_t topk, hipStream_t stream, char* ws, size_t ws_bytes);
 // One-launch gated decode (no workspace): the caller's block means, a gate
 // choice to make, at most 2048 past blocks and kDecFusedMaxKeys kept keys.
 constexpr int kDecFusedMaxKeys = 8192;

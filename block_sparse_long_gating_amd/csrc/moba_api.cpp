@@ -24,6 +24,9 @@ struct DeviceState {
   hipError_t init_error = hipSuccess;
   bool gfx950 = false;
   int num_cus = 0;
+  int device = 0;
+  std::once_flag pool_once;   // the workspace pool is created on the first call that needs one
+  hipError_t pool_error = hipSuccess;
   hipMemPool_t pool = nullptr;
 };
 
@@ -43,20 +46,24 @@ void init_device(int dev, DeviceState* st) {
   }
   st->gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
   st->num_cus = prop.multiProcessorCount;
+  st->device = dev;
+}
+
+void init_pool(DeviceState* st) {
   hipMemPoolProps props;
   std::memset(&props, 0, sizeof(props));
   props.allocType = hipMemAllocationTypePinned;
   props.handleTypes = hipMemHandleTypeNone;
   props.location.type = hipMemLocationTypeDevice;
-  props.location.id = dev;
-  e = hipMemPoolCreate(&st->pool, &props);
+  props.location.id = st->device;
+  hipError_t e = hipMemPoolCreate(&st->pool, &props);
   if (e != hipSuccess) {
-    st->init_error = e;
+    st->pool_error = e;
     return;
   }
   uint64_t keep = ~0ull;  // keep freed workspace in the pool across calls
   e = hipMemPoolSetAttribute(st->pool, hipMemPoolAttrReleaseThreshold, &keep);
-  if (e != hipSuccess) st->init_error = e;
+  if (e != hipSuccess) st->pool_error = e;
 }
 
 // Resolves the current device; returns a moba status.
@@ -198,6 +205,8 @@ moba::Workspace bind(const WsPlan& w, char* base, bool full) {
 }
 
 int alloc_ws(DeviceState* st, size_t bytes, hipStream_t stream, char** out) {
+  std::call_once(st->pool_once, init_pool, st);
+  if (st->pool_error != hipSuccess) return hip_fail(st->pool_error);
   void* p = nullptr;
   hipError_t e = hipMallocFromPoolAsync(&p, bytes ? bytes : 256, st->pool, stream);
   if (e == hipErrorOutOfMemory) {
@@ -438,9 +447,11 @@ int backward_impl(const void* q, const void* k, const void* v, const void* out, 
   return finish(e, base, stream);
 }
 
+// ext_ws: caller-provided workspace of ext_cap bytes (the allocation-free
+// entry point); nullptr takes it from the pool.
 int decode_impl(const void* q, const void* k, const void* v, const float* kbar, int32_t kbar_blocks, void* out,
                 float* lse, int32_t* sel, int64_t N, int32_t H, int32_t D, int32_t B, int32_t topk,
-                hipStream_t stream) {
+                hipStream_t stream, char* ext_ws = nullptr, size_t ext_cap = 0) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || lse == nullptr) return MOBA_ERR_INVALID_ARG;
   if (N < 1 || H < 1 || B < 1 || topk < 1) return MOBA_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return MOBA_ERR_UNSUPPORTED;
@@ -494,7 +505,16 @@ int decode_impl(const void* q, const void* k, const void* v, const float* kbar, 
   const size_t o_ml = L.add(static_cast<size_t>(H) * a.units * 2 * 4);
   const size_t o_kb = L.add(own_kbar ? static_cast<size_t>(H) * j * D * 4 : 0);
   char* base = nullptr;
-  if ((s = alloc_ws(st, L.total, stream, &base)) != MOBA_OK) return s;
+  if (ext_ws != nullptr) {
+    if (L.total > ext_cap) return MOBA_ERR_UNSUPPORTED;
+    base = ext_ws;
+    if (g_poison_workspace.load(std::memory_order_relaxed) != 0) {
+      const hipError_t pe = moba::launch_fill(base, L.total, 0xFFFFFFFFu, stream);
+      if (pe != hipSuccess) return hip_fail(pe);
+    }
+  } else if ((s = alloc_ws(st, L.total, stream, &base)) != MOBA_OK) {
+    return s;
+  }
   a.q = static_cast<const moba::bf16*>(q);
   a.k = static_cast<const moba::bf16*>(k);
   a.v = static_cast<const moba::bf16*>(v);
@@ -511,10 +531,23 @@ int decode_impl(const void* q, const void* k, const void* v, const float* kbar, 
   if (own_kbar)
     e = moba::launch_pool(k, false, reinterpret_cast<float*>(base + o_kb), nullptr, j * B, H, D, B, stream);
   if (e == hipSuccess) e = moba::launch_decode(a, stream);
+  if (ext_ws != nullptr) return e == hipSuccess ? MOBA_OK : hip_fail(e);
   return finish(e, base, stream);
 }
 
 }  // namespace
+
+namespace moba {
+
+int fail_hip(hipError_t e) { return hip_fail(e); }
+
+int decode_with_workspace(const void* q, const void* k, const void* v, const float* kbar, int32_t kbar_blocks,
+                          void* out, float* lse, int32_t* sel, int64_t N, int32_t H, int32_t D, int32_t block_size,
+                          int32_t topk, hipStream_t stream, char* ws, size_t ws_bytes) {
+  return decode_impl(q, k, v, kbar, kbar_blocks, out, lse, sel, N, H, D, block_size, topk, stream, ws, ws_bytes);
+}
+
+}  // namespace moba
 
 extern "C" {
 

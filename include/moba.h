@@ -261,6 +261,27 @@ int moba_decode_fwd(const void* q, const void* k, const void* v, const float* kb
                     int32_t block_size, int32_t topk, hipStream_t stream);
 
 /*
+ * moba_decode_fwd without any device allocation, for callers that cannot
+ * allocate: code under HIP graph capture, tight generation loops, harnesses
+ * that forbid hipMalloc. Same arguments, results and error behaviour as
+ * moba_decode_fwd (bit for bit), but its workspace is a fixed library array of
+ * MOBA_NOALLOC_SCRATCH_BYTES per GPU (held from the first call on that GPU
+ * until the process ends) instead of the stream-ordered pool; the call itself
+ * allocates and frees nothing. A step whose workspace would exceed that size
+ * (roughly H * units * (D + 2) * 4 bytes of partials plus H * j * (D + 2) * 4
+ * bytes of block means and scores when kbar is NULL; the one-launch gated step
+ * needs none) returns MOBA_ERR_UNSUPPORTED and enqueues nothing. All calls on
+ * one GPU share the array and it keeps the last call's contents (every byte a
+ * call reads it has written first): calls that may overlap on one GPU (other
+ * streams, or other threads without ordering) race and must be serialised by
+ * the caller; calls ordered on one stream are safe.
+ */
+#define MOBA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moba_decode_fwd_noalloc(const void* q, const void* k, const void* v, const float* kbar, int32_t kbar_blocks,
+                            void* out, float* lse, int32_t* sel, int64_t N, int32_t H, int32_t D,
+                            int32_t block_size, int32_t topk, hipStream_t stream);
+
+/*
  * Debug aid for the workspace (the lists, partial outputs and counters the
  * stages hand to each other, e.g. the regrouped query lists of the 智东西
  * report, section 二, implementation step 2). With `on` non-zero, every later
