@@ -130,14 +130,15 @@ constexpr int kInvInts = kAttnTile * kFusedMaxPast;
 constexpr int kInvRounds = kInvInts / (kWaves * kWave);
 
 // LDS image of one ring slot. A slot holds either one 64-key tile of K and V
-// (row-major, keys on rows) or 128 query rows. Rows are padded so that the
-// 16-byte operand reads of 16 consecutive rows (K, Q) and the 8-byte transpose
-// reads of 4 rows x 32 bytes (V) fall on distinct banks. The slot is filled in
+// (row-major, keys on rows) or 128 query rows. Rows are padded (K and Q by
+// 16 bytes, V by 32) so that the 16-byte operand reads of consecutive rows
+// (K, Q) fall on distinct banks; of the paddings tried for V (16, 32, 48
+// bytes) 32 gave the fastest past-block launch. The slot is filled in
 // 1 KB windows (one 16-byte load per lane); wave w takes windows w, w + 8, ...
 template <int D>
 struct Lay {
   static constexpr int kKStride = 2 * D + 16;
-  static constexpr int kVStride = 2 * D + (D == 128 ? 48 : 32);
+  static constexpr int kVStride = 2 * D + 32;
   static constexpr int kKBytes = kKTile * kKStride;
   static constexpr int kVBytes = kKTile * kVStride;
   static constexpr int kKSlots16 = kKStride / 16;   // 16-byte units per padded row
@@ -946,13 +947,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
         }
       }
       const int64_t tok = static_cast<int64_t>(cd.b) * a.B + cd.start + pos;
-      // Slots without a query write to the dump rows of the own-block buffers.
+      // Slots without a query write to the dump rows of the past-block partials.
       store_tile(o, 1.f / ww, [&](int ps) -> bf16* {
         return ps < cd.count ? a.out + ((static_cast<int64_t>(cd.b) * a.B + cd.start + ps) * a.H + cd.h) * D
-                             : a.part_diag + (static_cast<int64_t>(a.H) * a.N + ps) * D;
+                             : a.part_off + (a.p_off + ps) * D;
       });
-      store4(valid ? a.lse_out + static_cast<int64_t>(cd.h) * a.N + tok
-                   : a.lse_diag + static_cast<int64_t>(a.H) * a.N + pos,
+      store4(valid ? a.lse_out + static_cast<int64_t>(cd.h) * a.N + tok : a.lse_off + a.p_off + pos,
              (mm + log2f(ww)) * kLn2);
     } else {
       const float l_tot = l + __shfl_xor(l, 32);

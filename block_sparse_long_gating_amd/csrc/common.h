@@ -15,7 +15,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 // Queries per gate tile (4 waves x 32 queries).
 constexpr int kQTile = 128;
-// Queries per block-attention work item (4 waves x 64 queries).
+// Queries per block-attention work item (8 waves x 32 queries).
 constexpr int kAttnTile = 256;
 // Extra partial-output rows past the end of each partial buffer: work-item
 // slots without a query write there, so every lane of the attention kernel
@@ -47,6 +47,7 @@ struct Workspace {
   int32_t* cnt;         // [H*n][ntiles] per-tile off-diagonal counts -> exclusive prefix
   int32_t* totals;      // [H*n] off-diagonal list length of every (head, block)
   int32_t* offs;        // [H*n] global start of every (head, block) list
+  int32_t* istart;      // [H*n] first work item of every (head, block) list
   int32_t* rk;          // [H][N][Lmax] rank of a query inside its tile's share of a list
   int32_t* qidx;        // [P_off] query of every list entry
   int32_t* inv;         // [H][N][Lmax] list position of each off-diagonal selection

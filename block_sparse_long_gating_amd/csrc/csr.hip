@@ -6,11 +6,13 @@
 // that kept that block, ordered by query position:
 //   1. scan_tiles: per (head, block), exclusive prefix of the per-tile counts
 //      written by the gate, and the list length;
-//   2. build_lists (one 1024-thread workgroup): global start of every list and the work
-//      items of at most kAttnTile list entries each;
-//   3. scatter: every (query, kept past block) pair lands at
-//      start(list) + prefix(tile) + rank-in-tile; the position is also kept per
-//      query so the merge can find its partial outputs again.
+//   2. build_lists (one 1024-thread workgroup): global start of every list and
+//      of its work items (at most kAttnTile list entries each);
+//   3. scatter (one workgroup per query tile and head): every (query, kept
+//      past block) pair lands at start(list) + prefix(tile) + rank-in-tile,
+//      written as the tile's run of each list; the position is also kept per
+//      query so the merge can find its partial outputs again; and the work
+//      items.
 // Only integer arithmetic in fixed orders: the lists are deterministic.
 #include <algorithm>
 
@@ -73,10 +75,13 @@ __global__ __launch_bounds__(256) void scan_tiles_kernel(int32_t* __restrict__ c
 
 constexpr int kListThreads = 1024;
 
+// List starts and work-item starts of every (head, block): two exclusive
+// scans over the E list lengths (one workgroup; E = H * n is small), and the
+// number of work items. The items themselves are written by the scatter.
 __global__ __launch_bounds__(kListThreads) void build_lists_kernel(const int32_t* __restrict__ totals,
                                                                    int32_t* __restrict__ offs,
-                                                                   WorkItem* __restrict__ items,
-                                                                   int32_t* __restrict__ counters, int n, int64_t E) {
+                                                                   int32_t* __restrict__ istart,
+                                                                   int32_t* __restrict__ counters, int64_t E) {
   __shared__ int64_t sh[kListThreads / 64];
   const int64_t per = (E + kListThreads - 1) / kListThreads;
   const int64_t lo = min(E, static_cast<int64_t>(threadIdx.x) * per);
@@ -93,41 +98,98 @@ __global__ __launch_bounds__(kListThreads) void build_lists_kernel(const int32_t
   for (int64_t e = lo; e < hi; ++e) {
     const int64_t len = totals[e];
     offs[e] = static_cast<int32_t>(pos);
-    for (int64_t c = 0; c < len; c += kAttnTile) {
-      WorkItem w;
-      w.h = static_cast<int32_t>(e / n);
-      w.b = static_cast<int32_t>(e % n);
-      w.start = static_cast<int32_t>(pos + c);
-      w.count = static_cast<int32_t>(len - c < kAttnTile ? len - c : kAttnTile);
-      items[it++] = w;
-    }
+    istart[e] = static_cast<int32_t>(it);
     pos += len;
+    it += (len + kAttnTile - 1) / kAttnTile;
   }
   if (threadIdx.x == 0) counters[0] = static_cast<int32_t>(tot_items);
   if (threadIdx.x < kXcds) counters[kCursorStride * (1 + threadIdx.x)] = 0;
 }
 
+// One workgroup per (query tile, head). Every (query, kept past block) pair
+// of the tile lands at start(list) + prefix(tile) + rank-in-tile. The pairs
+// are first sorted by block in LDS (the tile's share of each list is one
+// contiguous run of the list), so the query indices leave in runs of
+// consecutive addresses; the list positions are written per query
+// (contiguous rows). The workgroup also writes the work items of the lists
+// b = tile, tile + ntiles, ... of its head.
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ sel, const int32_t* __restrict__ rk,
                                                       const int32_t* __restrict__ cnt,
-                                                      const int32_t* __restrict__ offs, int32_t* __restrict__ qidx,
-                                                      int32_t* __restrict__ inv, int64_t N, int H, int B, int n,
-                                                      int topk, int lmax, int ntiles, const int32_t* __restrict__ blo) {
-  const int64_t g = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (g >= N * H) return;
-  const int h = static_cast<int>(g / N);
-  const int64_t t = g % N;
-  const int j = static_cast<int>(t / B);
-  const int L = kept_past(j, blo != nullptr ? blo[j] : 0, topk);   // kept past blocks, ascending in sel
-  const int tile = static_cast<int>(t / kQTile);
-  const int32_t* srow = sel + g * topk;
-  const int32_t* rrow = rk + g * lmax;
-  int32_t* irow = inv + g * lmax;
-  for (int s = 0; s < L; ++s) {
-    const int b = srow[s];
-    const int64_t e = static_cast<int64_t>(h) * n + b;
-    const int32_t pos = offs[e] + cnt[e * ntiles + tile] + rrow[s];
-    qidx[pos] = static_cast<int32_t>(t);
-    irow[s] = pos;
+                                                      const int32_t* __restrict__ totals,
+                                                      const int32_t* __restrict__ offs,
+                                                      const int32_t* __restrict__ istart, int32_t* __restrict__ qidx,
+                                                      int32_t* __restrict__ inv, WorkItem* __restrict__ items,
+                                                      int64_t N, int H, int B, int n, int topk, int lmax, int ntiles,
+                                                      const int32_t* __restrict__ blo) {
+  extern __shared__ int32_t csm[];
+  __shared__ int64_t sh[4];
+  __shared__ int32_t s_total;
+  const int tile = static_cast<int>(blockIdx.x);
+  const int h = static_cast<int>(blockIdx.y);
+  const int tid = static_cast<int>(threadIdx.x);
+  const int64_t hn = static_cast<int64_t>(h) * n;
+
+  // Work items of this workgroup's lists.
+  for (int b = tile; b < n; b += ntiles) {
+    const int64_t e = hn + b;
+    const int len = totals[e];
+    const int i0 = istart[e], p0 = offs[e];
+    for (int c = tid; c * kAttnTile < len; c += 256) {
+      WorkItem wi;
+      wi.h = h;
+      wi.b = b;
+      wi.start = p0 + c * kAttnTile;
+      wi.count = min(kAttnTile, len - c * kAttnTile);
+      items[i0 + c] = wi;
+    }
+  }
+  if (lmax == 0) return;
+
+  const int64_t t0 = static_cast<int64_t>(tile) * kQTile;
+  const int64_t t1 = min(N, t0 + kQTile);
+  const int jmax = static_cast<int>((t1 - 1) / B);   // the tile's past blocks are all below its last block
+  if (jmax == 0) return;
+  // Per-block share of the tile (its count), then the exclusive prefix over blocks.
+  int32_t* const pre = csm;                                              // [jmax]
+  int2* const ent = reinterpret_cast<int2*>(csm + ((jmax + 3) & ~3));    // [kQTile * lmax]: (position, query)
+  const int per = (jmax + 255) / 256;
+  const int b0 = min(jmax, tid * per), b1 = min(jmax, b0 + per);
+  int64_t sum = 0;
+  for (int b = b0; b < b1; ++b) {
+    const int64_t e = hn + b;
+    const int c = (tile + 1 < ntiles ? cnt[e * ntiles + tile + 1] : totals[e]) - cnt[e * ntiles + tile];
+    pre[b] = c;
+    sum += c;
+  }
+  int64_t total;
+  int64_t run = block_exclusive_scan<256>(sum, sh, &total);
+  for (int b = b0; b < b1; ++b) {
+    const int c = pre[b];
+    pre[b] = static_cast<int32_t>(run);
+    run += c;
+  }
+  if (tid == 0) s_total = static_cast<int32_t>(total);
+  __syncthreads();
+  // Pairs in query order: coalesced reads of sel and rk and writes of inv.
+  const int nq = static_cast<int>(t1 - t0);
+  for (int i = tid; i < nq * lmax; i += 256) {
+    const int qi = i / lmax, s = i - qi * lmax;
+    const int64_t t = t0 + qi;
+    const int j = static_cast<int>(t / B);
+    if (s >= kept_past(j, blo != nullptr ? blo[j] : 0, topk)) continue;
+    const int64_t g = static_cast<int64_t>(h) * N + t;
+    const int b = sel[g * topk + s];
+    const int r = rk[g * lmax + s];
+    const int64_t e = hn + b;
+    const int32_t pos = offs[e] + cnt[e * ntiles + tile] + r;
+    inv[g * lmax + s] = pos;
+    ent[pre[b] + r] = make_int2(pos, static_cast<int32_t>(t));
+  }
+  __syncthreads();
+  const int tot = s_total;
+  for (int k = tid; k < tot; k += 256) {
+    const int2 x = ent[k];
+    qidx[x.x] = x.y;
   }
 }
 
@@ -136,11 +198,12 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
 hipError_t launch_csr(const Problem& p, const Workspace& ws, const int32_t* sel, hipStream_t stream) {
   const int64_t E = static_cast<int64_t>(p.H) * p.n;
   scan_tiles_kernel<<<static_cast<unsigned>(E), 256, 0, stream>>>(ws.cnt, ws.totals, p.ntiles);
-  build_lists_kernel<<<1, kListThreads, 0, stream>>>(ws.totals, ws.offs, ws.items, ws.counters, p.n, E);
-  const int64_t threads = p.N * p.H;
-  if (p.lmax > 0)
-    scatter_kernel<<<static_cast<unsigned>((threads + 255) / 256), 256, 0, stream>>>(
-        sel, ws.rk, ws.cnt, ws.offs, ws.qidx, ws.inv, p.N, p.H, p.B, p.n, p.topk, p.lmax, p.ntiles, p.blo);
+  build_lists_kernel<<<1, kListThreads, 0, stream>>>(ws.totals, ws.offs, ws.istart, ws.counters, E);
+  // LDS: the per-block prefix of a tile's past blocks (at most n) and its (position, query) pairs.
+  const size_t smem = static_cast<size_t>((p.n + 3) & ~3) * 4 + static_cast<size_t>(kQTile) * p.lmax * 8;
+  dim3 grid(static_cast<unsigned>(p.ntiles), static_cast<unsigned>(p.H));
+  scatter_kernel<<<grid, 256, smem, stream>>>(sel, ws.rk, ws.cnt, ws.totals, ws.offs, ws.istart, ws.qidx, ws.inv,
+                                              ws.items, p.N, p.H, p.B, p.n, p.topk, p.lmax, p.ntiles, p.blo);
   return hipGetLastError();
 }
 

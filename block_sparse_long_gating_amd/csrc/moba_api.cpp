@@ -140,8 +140,8 @@ struct Layout {
 
 // Workspace offsets for the requested stages.
 struct WsPlan {
-  size_t kbar, kpieces, cnt, totals, offs, rk, qidx, inv, items, counters, part_diag, lse_diag, part_off, lse_off,
-      sel, delta, part_dq, blo;
+  size_t kbar, kpieces, cnt, totals, offs, istart, rk, qidx, inv, items, counters, part_diag, lse_diag, part_off,
+      lse_off, sel, delta, part_dq, blo;
   size_t total;
 };
 
@@ -160,14 +160,17 @@ WsPlan plan(const moba::Problem& p, bool full, bool backward = false, bool packe
     w.cnt = L.add(hn * p.ntiles * 4);
     w.totals = L.add(hn * 4);
     w.offs = L.add(hn * 4);
+    w.istart = L.add(hn * 4);
     w.rk = L.add(hN * p.lmax * 4);
     w.qidx = L.add(p.p_off * 4);
     w.inv = L.add(hN * p.lmax * 4);
     w.items = L.add(p.max_items * sizeof(moba::WorkItem));
     w.counters = L.add(moba::kCounterInts * 4);
     if (!backward) {
-      w.part_diag = L.add((hN + moba::kDumpRows) * p.D * es);
-      w.lse_diag = L.add((hN + moba::kDumpRows) * 4);
+      // With the merge fused into the own-block pass there are no own-block partials.
+      const bool fused = moba::merge_fused(p);
+      w.part_diag = L.add(fused ? 0 : (hN + moba::kDumpRows) * p.D * es);
+      w.lse_diag = L.add(fused ? 0 : (hN + moba::kDumpRows) * 4);
       w.part_off = L.add((p.p_off + moba::kDumpRows) * p.D * es);
       w.lse_off = L.add((p.p_off + moba::kDumpRows) * 4);
     } else {
@@ -190,6 +193,7 @@ moba::Workspace bind(const WsPlan& w, char* base, bool full) {
     ws.cnt = reinterpret_cast<int32_t*>(base + w.cnt);
     ws.totals = reinterpret_cast<int32_t*>(base + w.totals);
     ws.offs = reinterpret_cast<int32_t*>(base + w.offs);
+    ws.istart = reinterpret_cast<int32_t*>(base + w.istart);
     ws.rk = reinterpret_cast<int32_t*>(base + w.rk);
     ws.qidx = reinterpret_cast<int32_t*>(base + w.qidx);
     ws.inv = reinterpret_cast<int32_t*>(base + w.inv);
