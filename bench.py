@@ -5,8 +5,9 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload h32]
 One step is one whole ``moba_prefill_fwd`` call (block mean-pool, gate and
 causal top-k, query lists, block attention, LSE merge) on inputs already
 resident in HBM, including the workspace taken from the library's stream-ordered
-pool. W untimed calls (default 100: the call time settles after ~60) precede
-the K timed ones, which run with nothing else on the stream. Prints one JSON
+pool. Untimed calls for --settle-ms of wall time (the shader clock ramps up
+over the first ~40 ms of load) and then W untimed warm-up calls precede the K
+timed ones, which run with nothing else on the stream. Prints one JSON
 line with the effective TFLOP/s (only the attended, causal (query, key) pairs
 of the selected blocks count, 4*D FLOPs each), the fraction of the bf16 MFMA
 peak, per-stage device times from HIP events the library records on its
@@ -327,7 +328,23 @@ def cpu_baseline(w, q, k, v, gpu_out, gpu_lse, gpu_sel, target_s: float):
     return res, res_parity
 
 
-def configs_bench(moba, names, steps: int, cpu_rows: int, with_cpu: bool):
+def settle(call, ms: float, min_calls: int = 3) -> int:
+    """Untimed calls until `ms` of wall time have passed (at least min_calls):
+    brings the shader clock to its loaded level. Returns the number of calls."""
+    import torch
+    torch.cuda.synchronize()
+    t_end = time.perf_counter() + ms * 1e-3
+    calls = 0
+    while calls < min_calls or time.perf_counter() < t_end:
+        call()
+        calls += 1
+        if calls % 10 == 0 or calls == min_calls:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return calls
+
+
+def configs_bench(moba, names, steps: int, cpu_rows: int, with_cpu: bool, settle_ms: float):
     """The whole prefill call on the other workloads (their own inputs),
     with the past-block kernel's launch time, and the oracle on a seeded row
     sample of the long ones (GPU parity on the same rows)."""
@@ -345,8 +362,7 @@ def configs_bench(moba, names, steps: int, cpu_rows: int, with_cpu: bool):
         out = torch.empty_like(qd)
         lse = torch.empty((w.H, w.N), dtype=torch.float32, device=dev)
         nsteps = steps if effective_pairs(w.N, w.block_size, w.topk) * w.H < 10 ** 10 else max(3, steps // 4)
-        for _ in range(3):
-            moba.prefill(qd, kd, vd, w.block_size, w.topk, out=out, lse=lse)
+        settle(lambda: moba.prefill(qd, kd, vd, w.block_size, w.topk, out=out, lse=lse), settle_ms)
         start = torch.cuda.Event(enable_timing=True)
         stop = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -405,9 +421,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    # The call time settles after ~60 calls (~70 ms of work at h32: clocks and
-    # the workspace pool reach their steady state); 100 untimed calls cover it.
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="h32")
     ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -425,6 +439,9 @@ def main():
                     help="other workloads to time after the headline one (comma list; 'none' for none)")
     ap.add_argument("--config-cpu-rows", type=int, default=1024,
                     help="oracle rows sampled per long workload for its CPU time and parity")
+    ap.add_argument("--settle-ms", type=float, default=150.0,
+                    help="before the warm-up calls, keep the GPU busy with prefill calls for this long (ms of wall "
+                         "time): the shader clock ramps up over the first ~40 ms of load")
     ap.add_argument("--per-call-ms", type=int, default=0,
                     help="before the warm-up, time this many single calls with HIP events (prints them)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -470,6 +487,16 @@ def main():
         torch.cuda.synchronize()
         times = [a.elapsed_time(b) for a, b in evs]
         print("[bench] per-call ms: " + " ".join(f"{t:.3f}" for t in times), file=sys.stderr, flush=True)
+
+    # Clock settle: the shader clock rises from ~1.8 to ~2.3 GHz over the first
+    # ~40 ms of continuous load while every kernel's cycle count stays the same
+    # (per-dispatch GRBM_GUI_ACTIVE against the dispatch time), so the first
+    # calls of a process measure the power state, not the code. Prefill calls
+    # run until settle_ms of wall time have passed; they are reported.
+    settle_calls = 0
+    if args.settle_ms > 0:
+        settle_calls = settle(lambda: moba.prefill(qd, kd, vd, w.block_size, w.topk, out=out, lse=lse),
+                              args.settle_ms, min_calls=1)
 
     for _ in range(args.warmup):
         moba.prefill(qd, kd, vd, w.block_size, w.topk, out=out, lse=lse)
@@ -542,6 +569,9 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle": {"calls": settle_calls, "ms": args.settle_ms,
+                         "why": "untimed prefill calls before the warm-up: the shader clock ramps from ~1.8 to "
+                                "~2.3 GHz over the first ~40 ms of load (kernel cycle counts constant)"},
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
@@ -614,7 +644,8 @@ def main():
     if names:
         del qd, kd, vd, out, lse
         torch.cuda.empty_cache()
-        result["configs"] = configs_bench(moba, names, args.steps, args.config_cpu_rows, args.cpu_baseline == "on")
+        result["configs"] = configs_bench(moba, names, args.steps, args.config_cpu_rows, args.cpu_baseline == "on",
+                                          args.settle_ms)
     print(json.dumps(result), flush=True)
 
 
