@@ -603,6 +603,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
     kvoff[u] = static_cast<uint32_t>(row) * row_bytes + 16u * ch;
   }
   vmask = uniform_u32(vmask);
+  // Past-block items: row (within a 128-row Q tile) and byte offset in that
+  // row of each of the lane's Q loads; units past the tile's rows or chunks
+  // reload the tile's last row or a row's first chunk.
+  int qrow[kCausal ? 1 : L::kRoundsHi], qch16[kCausal ? 1 : L::kRoundsHi];
+  if (!kCausal) {
+#pragma unroll
+    for (int u = 0; u < L::kRoundsHi; ++u) {
+      const int s16 = (u * kWaves + w) * 64 + lane;
+      const int r = s16 / L::kKSlots16, ch = s16 % L::kKSlots16;
+      qrow[u] = r < kQTileRows ? r : kQTileRows - 1;
+      qch16[u] = 16 * (ch < L::kChunks ? ch : 0);
+    }
+  }
   const uint32_t ring_lds = lds_addr(ring);
   const uint32_t qbuf_lds = lds_addr(qbuf);
 
@@ -638,6 +651,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
       for (int u = 0; u < L::kRoundsHi; ++u)
         if (u >= u0 && u < u1 && (u < L::kRoundsLo || hi_rounds))
           dma16(m0base + u * kWaves * 1024, kvoff[u], ((vmask >> u) & 1) ? vb : kb);
+    } else if (!kCausal) {
+      // Past-block items: the lane's rows and chunk offsets of a Q tile come
+      // from the per-kernel table (row qrow[u] of the tile, i.e. item position
+      // 128 j + qrow[u]); the query index comes from the list entries in LDS.
+      const int32_t* qi_lds = qbuf + qb * kQBuf;
+      const uint64_t qh = uniform_ptr(a.q + static_cast<int64_t>(d.h) * D);
+#pragma unroll
+      for (int u = 0; u < L::kRoundsHi; ++u) {
+        if (u >= u0 && u < u1 && (u < L::kRoundsLo || hi_rounds)) {
+          const int pos = min(kQTileRows * j + qrow[u], d.count - 1);
+          const uint64_t tok = static_cast<uint32_t>(qi_lds[pos]);
+          dma16_addr(m0base + u * kWaves * 1024,
+                     reinterpret_cast<const void*>(qh + tok * row_bytes + static_cast<uint32_t>(qch16[u])));
+        }
+      }
     } else {
       const int32_t* qi_lds = qbuf + qb * kQBuf;
       // Opaque copy of the lane index: keeps the per-lane address arithmetic

@@ -10,8 +10,8 @@
 //
 // One workgroup per (block, group of up to 8 heads). Each thread owns 8
 // consecutive dims of one head on a strided subset of the block's rows
-// (16-byte loads; the group's heads of one token are one contiguous run), sums
-// them in fp64 in a fixed order, and the per-row-group partial sums are
+// (16-byte loads, two batches of eight rows in flight; the group's heads of
+// one token are one contiguous run), sums them in fp64 in a fixed order, and the per-row-group partial sums are
 // combined in LDS in a fixed order, so the result is deterministic and,
 // whenever the fp64 sum is exact, the correctly rounded mean.
 // The bf16 path also writes the exact 3-way bf16 split (hi + mid + lo == fp32
@@ -23,23 +23,34 @@ namespace moba {
 
 namespace {
 
+// Eight consecutive values of one row as loaded (one 16-byte load for bf16,
+// two for fp32), widened to float on use.
 template <typename T>
-__device__ __forceinline__ void load8(const T* p, float (&x)[8]);
+struct Raw8;
 
 template <>
-__device__ __forceinline__ void load8<bf16>(const bf16* p, float (&x)[8]) {
-  const bf16x8 v = load_bf16x8(p);
+struct Raw8<bf16> {
+  uint4 v;
+  __device__ __forceinline__ void load(const bf16* p) { v = load_u4(p); }
+  __device__ __forceinline__ void widen(float (&x)[8]) const {
+    const bf16x8 b = __builtin_bit_cast(bf16x8, v);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = static_cast<float>(v[e]);
-}
+    for (int e = 0; e < 8; ++e) x[e] = static_cast<float>(b[e]);
+  }
+};
 
 template <>
-__device__ __forceinline__ void load8<float>(const float* p, float (&x)[8]) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-}
+struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void widen(float (&x)[8]) const {
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+};
 
 template <typename T, int D, int kMode>
 __global__ __launch_bounds__(256) void pool_keys_kernel(const T* __restrict__ k, const float* __restrict__ weights,
@@ -82,19 +93,39 @@ __global__ __launch_bounds__(256) void pool_keys_kernel(const T* __restrict__ k,
     }
   };
 
-  // Eight independent 16-byte loads in flight per thread, added in row order.
-  int r = r0;
-  for (; r + 7 * rows_per_pass < B; r += 8 * rows_per_pass) {
-    float x[8][8];
+  // Rows in batches of eight, added in row order; the next batch's loads are
+  // in flight while the current one is added (two batches of registers).
+  const int rows = r0 < B ? (B - r0 + rows_per_pass - 1) / rows_per_pass : 0;   // this thread's rows
+  const int batches = rows / 8;
+  auto load_batch = [&](Raw8<T> (&buf)[8], int bt) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) load8<T>(base + static_cast<int64_t>(r + u * rows_per_pass) * row_stride, x[u]);
+    for (int u = 0; u < 8; ++u)
+      buf[u].load(base + static_cast<int64_t>(r0 + (8 * bt + u) * rows_per_pass) * row_stride);
+  };
+  auto add_batch = [&](const Raw8<T> (&buf)[8], int bt) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) add(x[u], r + u * rows_per_pass);
+    for (int u = 0; u < 8; ++u) {
+      float x[8];
+      buf[u].widen(x);
+      add(x, r0 + (8 * bt + u) * rows_per_pass);
+    }
+  };
+  Raw8<T> b0[8], b1[8];
+  if (batches > 0) load_batch(b0, 0);
+  for (int bt = 0; bt < batches; bt += 2) {
+    if (bt + 1 < batches) load_batch(b1, bt + 1);
+    add_batch(b0, bt);
+    if (bt + 1 < batches) {
+      if (bt + 2 < batches) load_batch(b0, bt + 2);
+      add_batch(b1, bt + 1);
+    }
   }
-  for (; r < B; r += rows_per_pass) {
-    float x0[8];
-    load8<T>(base + static_cast<int64_t>(r) * row_stride, x0);
-    add(x0, r);
+  for (int rr = 8 * batches; rr < rows; ++rr) {
+    Raw8<T> one;
+    one.load(base + static_cast<int64_t>(r0 + rr * rows_per_pass) * row_stride);
+    float x[8];
+    one.widen(x);
+    add(x, r0 + rr * rows_per_pass);
   }
 
 #pragma unroll
