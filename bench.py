@@ -42,6 +42,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -92,16 +93,25 @@ def device_info():
     return info
 
 
+def code_sha256(path: str) -> str:
+    """sha256 of a C++/HIP source with its comments and blank lines removed, so
+    that it changes with the code and not with the comments."""
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*$", "", line).rstrip() for line in text.splitlines()]
+    return hashlib.sha256("\n".join(line for line in lines if line).encode()).hexdigest()
+
+
 def traffic_for(workload: str):
     """HBM bytes per launch of the past-block attention kernel from the
     committed rocprofv3 counter summary, if it was taken on this workload with
-    the current kernel source (else None)."""
+    the current kernel code (else None)."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
-    src_hash = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
-    if t.get("attn_source_sha256") != src_hash or t.get("workload") != workload:
+    if t.get("attn_code_sha256") != code_sha256(ATTN_SRC) or t.get("workload") != workload:
         return None
     return t.get("bytes_per_launch")
 

@@ -14,7 +14,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["prefill", "gate_topk", "block_mean_keys", "MobaError", "library_path", "load_library",
+__all__ = ["prefill", "gate_topk", "block_mean_keys", "block_query_lists", "MobaError", "library_path", "load_library",
            "StageEvents", "STAGES", "STATUS", "MAX_TOPK", "MAX_BLOCKS", "debug_poison_workspace"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,6 +35,7 @@ _SIGNATURES = {
     "moba_block_mean_keys_f32": [_P, _P, _I64, _I32, _I32, _I32, _P],
     "moba_gate_topk": [_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P],
     "moba_gate_topk_f32": [_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P],
+    "moba_block_query_lists": [_P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _P],
     "moba_prefill_fwd": [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P],
     "moba_prefill_fwd_f32": [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P],
     "moba_prefill_fwd_timed": [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P],
@@ -147,6 +148,30 @@ def gate_topk(q, k, block_size: int, topk: int):
     _check(fn(q.data_ptr(), k.data_ptr(), sel.data_ptr(), N, H, D, block_size, topk, _stream(q.device)),
            "moba_gate_topk")
     return sel
+
+
+def block_query_lists(q, k, block_size: int, topk: int):
+    """The prefill's selection and its per-block query lists.
+
+    Returns ``(sel, offs, qidx)``: ``sel`` int32 ``[H, N, topk]`` as
+    ``gate_topk``; list ``(h, b)`` is ``qidx[offs[h*n + b]:offs[h*n + b + 1]]``,
+    the ascending positions of the queries that chose ``b`` as a past block.
+    """
+    import torch
+    N, H, D, f32 = _check_qkv(q, k)
+    if f32:
+        raise TypeError("block_query_lists takes bfloat16 q and k")
+    lib = load_library()
+    n = N // block_size if block_size > 0 and N % block_size == 0 else 0
+    # Buffer size: every query of block j keeps min(topk - 1, j) past blocks.
+    pairs = H * sum(block_size * min(topk - 1, j) for j in range(n)) if topk >= 1 else 0
+    sel = torch.empty((H, N, max(topk, 1)), dtype=torch.int32, device=q.device)
+    offs = torch.empty((H * n + 1,), dtype=torch.int32, device=q.device)
+    qidx = torch.empty((max(pairs, 1),), dtype=torch.int32, device=q.device)
+    _check(lib.moba_block_query_lists(q.data_ptr(), k.data_ptr(), sel.data_ptr(), offs.data_ptr(), qidx.data_ptr(),
+                                      pairs, N, H, D, block_size, topk, _stream(q.device)),
+           "moba_block_query_lists")
+    return sel, offs, qidx[:pairs]
 
 
 STAGES = ("pool", "gate", "lists", "attn_past", "attn_own", "merge")

@@ -4,28 +4,32 @@
 //   * past-block items: queries gathered from the block's query list; no mask;
 //   * own-block items: a run of consecutive queries of the block itself, with
 //     the causal mask inside the block (keys up to the query's own position).
-// Each item writes, per query, the softmax-normalised partial output over its
-// keys and the partial log-sum-exp; the merge kernel combines them.
+// Each past-block item writes, per query, the softmax-normalised partial
+// output over its keys and the partial log-sum-exp. The LSE merge of those
+// partials runs inside the own-block items when every query keeps at most
+// kFusedMaxPast past blocks, else in the merge kernel after both passes.
 //
 // bf16 kernel (gfx950): 8 waves per workgroup (two per SIMD), each wave owns
-// one 32-query column block, 64-key tiles of K and V staged row-major in LDS
-// (padded rows, double buffered through registers). Per wave and 32-key half
-// tile:
+// one 32-query column block of the item's 256 queries. Q tiles and the 64-key
+// K and V tiles are brought straight from HBM into LDS by buffer-to-LDS loads
+// (global_load_lds_dwordx4) through a 3-slot ring whose loads run two steps
+// ahead, across item boundaries. Per wave and 32-key half tile:
 //   S^T = K Q^T   v_mfma_f32_32x32x16_bf16, keys on the rows and queries on
 //                 the columns; Q stays in registers as the B operand;
 //   softmax       in registers per query column, exp2 with the 1/sqrt(D)
-//                 scale folded into one FMA; the running maximum is only
-//                 refreshed (and O rescaled) when it grows by more than 2^8,
-//                 which keeps every exponent <= 8 and is exact after the final
-//                 normalisation;
+//                 scale folded into one FMA against a running reference; the
+//                 reference is only raised (and O rescaled) when a half's
+//                 probabilities sum past 2^64 or are not finite, which is
+//                 rare and exact after the final normalisation;
 //   O^T += V^T P^T  P stays in registers as the B operand; the V^T operand is
 //                 read with ds_read_b64_tr_b16 (LDS transpose read) in the key
 //                 order the S accumulator layout hands to P.
-// Workgroups are persistent; each XCD walks its own contiguous share of the
-// item list through an atomic cursor, so the items of one key block run close
-// together on one L2.
+// The schedule is static and XCD-aware: each XCD takes a contiguous share of
+// the past-block items, so the items of one key block run close together on
+// one L2 (details above the kernel).
 //
-// fp32 kernel: one thread per query, K/V tiles in LDS, fp32 FMA throughout.
+// fp32 kernel: one thread per query, K/V tiles in LDS, fp32 FMA throughout;
+// its workgroups take items through a per-XCD atomic cursor.
 #include "common.h"
 #include "kernels.h"
 

@@ -46,7 +46,7 @@ struct Workspace {
   bf16* kpieces;        // [H][n][3][D] bf16 exact 3-way split of kbar (bf16 path)
   int32_t* cnt;         // [H*n][ntiles] per-tile off-diagonal counts -> exclusive prefix
   int32_t* totals;      // [H*n] off-diagonal list length of every (head, block)
-  int32_t* offs;        // [H*n] global start of every (head, block) list
+  int32_t* offs;        // [H*n + 1] global start of every (head, block) list, then the total
   int32_t* istart;      // [H*n] first work item of every (head, block) list
   int32_t* rk;          // [H][N][Lmax] rank of a query inside its tile's share of a list
   int32_t* qidx;        // [P_off] query of every list entry

@@ -76,8 +76,9 @@ __global__ __launch_bounds__(256) void scan_tiles_kernel(int32_t* __restrict__ c
 constexpr int kListThreads = 1024;
 
 // List starts and work-item starts of every (head, block): two exclusive
-// scans over the E list lengths (one workgroup; E = H * n is small), and the
-// number of work items. The items themselves are written by the scatter.
+// scans over the E list lengths (one workgroup; E = H * n is small), the total
+// list length (offs[E]) and the number of work items. The items themselves
+// are written by the scatter.
 __global__ __launch_bounds__(kListThreads) void build_lists_kernel(const int32_t* __restrict__ totals,
                                                                    int32_t* __restrict__ offs,
                                                                    int32_t* __restrict__ istart,
@@ -102,7 +103,10 @@ __global__ __launch_bounds__(kListThreads) void build_lists_kernel(const int32_t
     pos += len;
     it += (len + kAttnTile - 1) / kAttnTile;
   }
-  if (threadIdx.x == 0) counters[0] = static_cast<int32_t>(tot_items);
+  if (threadIdx.x == 0) {
+    counters[0] = static_cast<int32_t>(tot_items);
+    offs[E] = static_cast<int32_t>(tot_len);
+  }
   if (threadIdx.x < kXcds) counters[kCursorStride * (1 + threadIdx.x)] = 0;
 }
 

@@ -7,8 +7,9 @@
 // index; future blocks are never scored (wzjinhao.cn MoBA article, section 3,
 // causal_mask and current_block_force). Rows with j < topk keep all of 0..j.
 //
-// bf16 path: persistent workgroups of 8 waves x 32 queries, each owning one
-// head and walking pairs of 128-query tiles. The scores of 32 blocks x 32
+// bf16 path: persistent workgroups of 4 waves x 32 queries (one 128-query
+// tile at a time), each owning one head and walking every grid.x-th tile of
+// it. The scores of 32 blocks x 32
 // queries come from bf16 MFMA (v_mfma_f32_32x32x16_bf16) with the block means
 // as the A operand (rows = blocks) and the queries as the B operand (columns =
 // queries), so each lane ends up holding 16 block scores of one query. The

@@ -145,39 +145,45 @@ struct WsPlan {
   size_t total;
 };
 
-// `full`: the query lists and the forward partials; `backward`: the query
-// lists and the backward's Δ and dQ partials instead of the forward partials.
-WsPlan plan(const moba::Problem& p, bool full, bool backward = false, bool packed = false) {
+// What a call runs after the gate: nothing (gate only), the query lists
+// alone, the lists and the forward partials, or the lists and the backward's
+// Delta and dQ partials.
+enum class Stages { gate, lists, forward, backward };
+
+// Workspace offsets for the requested stages. With Stages::lists the caller
+// owns sel, offs and qidx, so the workspace holds none of them.
+WsPlan plan(const moba::Problem& p, Stages stages, bool packed = false) {
   Layout L;
   WsPlan w;
   std::memset(&w, 0, sizeof(w));
   const int64_t hn = static_cast<int64_t>(p.H) * p.n;
   const int64_t hN = static_cast<int64_t>(p.H) * p.N;
   const size_t es = p.is_f32 ? 4 : 2;
+  const bool own_lists = stages != Stages::lists;
   w.kbar = L.add(hn * p.D * 4);
   w.kpieces = L.add(p.is_f32 ? 0 : hn * 3 * p.D * 2);
-  if (full) {
+  if (stages != Stages::gate) {
     w.cnt = L.add(hn * p.ntiles * 4);
     w.totals = L.add(hn * 4);
-    w.offs = L.add(hn * 4);
+    w.offs = L.add(own_lists ? (hn + 1) * 4 : 0);   // list starts, then the total
     w.istart = L.add(hn * 4);
     w.rk = L.add(hN * p.lmax * 4);
-    w.qidx = L.add(p.p_off * 4);
+    w.qidx = L.add(own_lists ? p.p_off * 4 : 0);
     w.inv = L.add(hN * p.lmax * 4);
     w.items = L.add(p.max_items * sizeof(moba::WorkItem));
     w.counters = L.add(moba::kCounterInts * 4);
-    if (!backward) {
+    if (stages == Stages::forward) {
       // With the merge fused into the own-block pass there are no own-block partials.
       const bool fused = moba::merge_fused(p);
       w.part_diag = L.add(fused ? 0 : (hN + moba::kDumpRows) * p.D * es);
       w.lse_diag = L.add(fused ? 0 : (hN + moba::kDumpRows) * 4);
       w.part_off = L.add((p.p_off + moba::kDumpRows) * p.D * es);
       w.lse_off = L.add((p.p_off + moba::kDumpRows) * 4);
-    } else {
+    } else if (stages == Stages::backward) {
       w.delta = L.add(hN * 4);
       w.part_dq = L.add(p.p_off * p.D * 4);
     }
-    w.sel = L.add(hN * p.topk * 4);
+    w.sel = L.add(own_lists ? hN * p.topk * 4 : 0);
   }
   if (packed) w.blo = L.add(static_cast<size_t>(p.n) * 4);
   w.total = L.total;
@@ -319,7 +325,7 @@ int gate_impl(const void* q, const void* k, int32_t* sel, int64_t N, int32_t H, 
   moba::Problem p = make_problem(N, H, D, B, topk, is_f32);
   if (pk != nullptr) apply_packed(*pk, &p);
   p.topk = topk;   // the caller's rows are topk wide (entries past j + 1 are -1)
-  const WsPlan w = plan(p, false, false, pk != nullptr);
+  const WsPlan w = plan(p, Stages::gate, pk != nullptr);
   char* base = nullptr;
   if ((s = alloc_ws(st, w.total, stream, &base)) != MOBA_OK) return s;
   moba::Workspace ws = bind(w, base, false);
@@ -332,6 +338,35 @@ int gate_impl(const void* q, const void* k, int32_t* sel, int64_t N, int32_t H, 
   if (e == hipSuccess)
     e = moba::launch_pool(k, is_f32, ws.kbar, is_f32 ? nullptr : ws.kpieces, N, H, D, B, stream, pl.mode, pl.weights);
   if (e == hipSuccess) e = moba::launch_gate(p, q, ws, sel, false, st->num_cus, stream);
+  return finish(e, base, stream);
+}
+
+// Pooling, gate and the query lists of the prefill, with the lists written
+// into the caller's offs / qidx and the selection into the caller's sel.
+int query_lists_impl(const void* q, const void* k, int32_t* sel, int32_t* offs, int32_t* qidx, int64_t qidx_len,
+                     int64_t N, int32_t H, int32_t D, int32_t B, int32_t topk, hipStream_t stream) {
+  if (q == nullptr || k == nullptr || sel == nullptr || offs == nullptr || qidx == nullptr) return MOBA_ERR_INVALID_ARG;
+  int s = check_shape(N, H, D, B);
+  if (s != MOBA_OK) return s;
+  if ((s = check_topk(N, B, topk)) != MOBA_OK) return s;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(sel) || !aligned16(offs) || !aligned16(qidx))
+    return MOBA_ERR_UNSUPPORTED;
+  moba::Problem p = make_problem(N, H, D, B, topk, false);
+  if (p.p_off >= (int64_t{1} << 31)) return MOBA_ERR_UNSUPPORTED;
+  if (qidx_len < p.p_off) return MOBA_ERR_INVALID_ARG;
+  p.topk = topk;   // the caller's rows are topk wide (entries past j + 1 are -1)
+  DeviceState* st = nullptr;
+  if ((s = current_device(&st)) != MOBA_OK) return s;
+  const WsPlan w = plan(p, Stages::lists);
+  char* base = nullptr;
+  if ((s = alloc_ws(st, w.total, stream, &base)) != MOBA_OK) return s;
+  moba::Workspace ws = bind(w, base, true);
+  ws.offs = offs;
+  ws.qidx = qidx;
+  ws.sel = sel;
+  hipError_t e = moba::launch_pool(k, false, ws.kbar, ws.kpieces, N, H, D, B, stream, MOBA_POOL_MEAN, nullptr);
+  if (e == hipSuccess) e = moba::launch_gate(p, q, ws, sel, true, st->num_cus, stream);
+  if (e == hipSuccess) e = moba::launch_csr(p, ws, sel, stream);
   return finish(e, base, stream);
 }
 
@@ -355,7 +390,7 @@ int prefill_impl(const void* q, const void* k, const void* v, void* out, float* 
   if (p.p_off >= (int64_t{1} << 31)) return MOBA_ERR_UNSUPPORTED;
   DeviceState* st = nullptr;
   if ((s = current_device(&st)) != MOBA_OK) return s;
-  const WsPlan w = plan(p, true, false, pk != nullptr);
+  const WsPlan w = plan(p, Stages::forward, pk != nullptr);
   char* base = nullptr;
   if ((s = alloc_ws(st, w.total, stream, &base)) != MOBA_OK) return s;
   moba::Workspace ws = bind(w, base, true);
@@ -400,7 +435,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* out, 
   if (p.p_off >= (int64_t{1} << 31)) return MOBA_ERR_UNSUPPORTED;
   DeviceState* st = nullptr;
   if ((s = current_device(&st)) != MOBA_OK) return s;
-  const WsPlan w = plan(p, true, true, pk != nullptr);
+  const WsPlan w = plan(p, Stages::backward, pk != nullptr);
   char* base = nullptr;
   if ((s = alloc_ws(st, w.total, stream, &base)) != MOBA_OK) return s;
   moba::Workspace ws = bind(w, base, true);
@@ -573,6 +608,12 @@ int moba_gate_topk(const void* q, const void* k, int32_t* sel, int64_t N, int32_
 int moba_gate_topk_f32(const float* q, const float* k, int32_t* sel, int64_t N, int32_t H, int32_t D,
                        int32_t block_size, int32_t topk, hipStream_t stream) {
   return gate_impl(q, k, sel, N, H, D, block_size, topk, stream, true);
+}
+
+int moba_block_query_lists(const void* q, const void* k, int32_t* sel, int32_t* offs, int32_t* qidx,
+                           int64_t qidx_len, int64_t N, int32_t H, int32_t D, int32_t block_size, int32_t topk,
+                           hipStream_t stream) {
+  return query_lists_impl(q, k, sel, offs, qidx, qidx_len, N, H, D, block_size, topk, stream);
 }
 
 int moba_prefill_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int64_t N, int32_t H,

@@ -105,6 +105,30 @@ int moba_gate_topk_f32(const float* q, const float* k, int32_t* sel, int64_t N, 
                        int32_t D, int32_t block_size, int32_t topk, hipStream_t stream);
 
 /*
+ * Query lists only: the pooling, gate and regrouping stages of
+ * moba_prefill_fwd, with the regrouped queries handed back. Attention runs
+ * block by block over the queries that chose each block (智东西 report,
+ * section 二, implementation steps 1-2: queries reordered by their block
+ * assignment); a query's own block is not listed, since its queries are that
+ * block's own tokens.
+ *   sel  : int32 [H][N][topk], written as by moba_gate_topk.
+ *   offs : int32 [H * n + 1]. List (h, b) is qidx[offs[h*n + b] ..
+ *          offs[h*n + b + 1]); offs[H * n] = P, the total number of
+ *          (query, past block) pairs.
+ *   qidx : int32 [qidx_len]; entry = query position t of a query with
+ *          b in sel(t) and b < t / block_size; each list ascending, lists in
+ *          (h, b) order. P = H * sum over blocks j of block_size *
+ *          min(topk - 1, j) (a closed form the caller sizes qidx with);
+ *          qidx_len < P is MOBA_ERR_INVALID_ARG, entries past P are not written.
+ * bf16 q, k only. P >= 2^31 is MOBA_ERR_UNSUPPORTED. offs and qidx need 16-byte
+ * alignment like every other pointer. The lists are integer work in fixed
+ * orders: for a given sel they are bitwise reproducible.
+ */
+int moba_block_query_lists(const void* q, const void* k, int32_t* sel, int32_t* offs, int32_t* qidx,
+                           int64_t qidx_len, int64_t N, int32_t H, int32_t D, int32_t block_size, int32_t topk,
+                           hipStream_t stream);
+
+/*
  * Block pooling variants. The gate scores each past block through one
  * representative key; the pages pool by the mean (wzjinhao.cn MoBA article,
  * section 3, score_pooling = mean) and suggest trying max or weighted pooling

@@ -16,6 +16,7 @@ from .moba_oracle import (  # noqa: F401
     n_blocks,
     pooled_keys,
     pooled_keys_fp32,
+    query_lists,
     select_blocks,
     select_row,
     sparsity,

@@ -55,6 +55,9 @@ A(t) (the textbook softmax Jacobian).
 independent sequences (token offsets ``cu_seqlens``, each length a multiple of
 B) and apply the single-sequence definitions to each one.
 
+``query_lists`` regroups a selection into per-block lists of the queries
+that chose each past block (the reordering of 智东西 section 二, steps 1-2).
+
 ``moba_decode_ref`` is the generation step after the prefill: the newest token
 (position N - 1 of a cache whose length need not be a multiple of B, so its
 own block may be partial) gated and attended exactly like a prefill row; with
@@ -190,6 +193,38 @@ def select_blocks(q: np.ndarray, k: np.ndarray, block_size: int, topk: int,
                     row = sorted(order[i, :topk - 1].tolist() + [int(j)])
                 sel[h, c0 + i, :len(row)] = row
     return sel, kbar32
+
+
+def query_lists(sel: np.ndarray, block_size: int):
+    """Queries regrouped by the past block they chose.
+
+    Attention runs block by block over the queries routed to each block once
+    the queries are reordered by their block assignment (智东西 report,
+    section 二, implementation steps 1-2). For every head h and block b, in
+    (h, b) order, the list holds the query positions t, ascending, whose
+    selection row sel[h, t] contains b as a past block (b < t // block_size);
+    a query's own block is left out, its queries being that block's tokens.
+
+    Returns (offs, qidx): list (h, b) is qidx[offs[h*n + b]:offs[h*n + b + 1]],
+    offs int64 [H*n + 1], qidx int32.
+    """
+    H, N, _ = sel.shape
+    n = n_blocks(N, block_size)
+    lists = [[[] for _ in range(n)] for _ in range(H)]
+    for h in range(H):
+        for t in range(N):                      # ascending t: every list comes out ascending
+            j = t // block_size
+            for b in sel[h, t]:
+                b = int(b)
+                if 0 <= b < j:
+                    lists[h][b].append(t)
+    offs = [0]
+    qidx: list[int] = []
+    for h in range(H):
+        for b in range(n):
+            qidx.extend(lists[h][b])
+            offs.append(len(qidx))
+    return np.asarray(offs, np.int64), np.asarray(qidx, np.int32)
 
 
 def attended_keys(sel_row, t: int, block_size: int) -> np.ndarray:

@@ -286,6 +286,44 @@ def pin_closed_form_pairs(m):
         assert all(len(m.attended_keys(sel[0, t], t, B)) == m.attended_count(t, B, topk) for t in range(N))
 
 
+def pin_query_lists_hand_example(m):
+    """Lists regrouped by hand from two hand-written selections (N = 8, B = 2,
+    top-2): list (h, b) holds the queries t that chose b as a past block."""
+    sel = np.array([
+        [[0, -1], [0, -1], [0, 1], [0, 1], [1, 2], [0, 2], [2, 3], [0, 3]],
+        [[0, -1], [0, -1], [0, 1], [0, 1], [0, 2], [0, 2], [1, 3], [1, 3]],
+    ], np.int32)
+    offs, qidx = m.query_lists(sel, 2)
+    assert offs.tolist() == [0, 4, 5, 6, 6, 10, 12, 12, 12]
+    assert qidx.tolist() == [2, 3, 5, 7, 4, 6, 2, 3, 4, 5, 6, 7]
+    # topk wider than the eligible blocks: the -1 padding lists nothing.
+    offs, qidx = m.query_lists(np.array([[[0, -1, -1], [0, -1, -1], [0, 1, -1], [0, 1, -1]]], np.int32), 2)
+    assert offs.tolist() == [0, 2, 2] and qidx.tolist() == [2, 3]
+
+
+def pin_query_lists_transpose(m):
+    """On oracle selections: the lists are the transpose of the selection minus
+    the own block (checked through a membership matrix), each list ascending,
+    and the total is the closed form H * sum_j B * min(k - 1, j)."""
+    for N, H, B, topk in [(96, 2, 8, 3), (128, 3, 16, 20), (64, 1, 8, 1), (160, 2, 32, 2)]:
+        q, k, _ = _rand(N, H, 4, 131)
+        sel, _ = m.select_blocks(q, k, B, topk)
+        offs, qidx = m.query_lists(sel, B)
+        n = N // B
+        assert offs.shape == (H * n + 1,) and offs[0] == 0
+        assert offs[-1] == H * sum(B * min(topk - 1, j) for j in range(n)) == qidx.shape[0]
+        member = np.zeros((H, N, n), bool)
+        for e in range(H * n):
+            lst = qidx[offs[e]:offs[e + 1]]
+            assert np.all(np.diff(lst) > 0)
+            assert not member[e // n, lst, e % n].any()
+            member[e // n, lst, e % n] = True
+        for h in range(H):
+            for t in range(N):
+                want = {int(b) for b in sel[h, t] if 0 <= b < t // B}
+                assert set(np.flatnonzero(member[h, t]).tolist()) == want
+
+
 def pin_lse_merge(m):
     """Merging per-block softmax partials by log-sum-exp equals the oracle's one softmax."""
     N, H, D, B, topk = 96, 2, 8, 8, 4
@@ -673,7 +711,8 @@ def pin_varlen_one_sequence_and_order(m):
 ALL_PINS = [
     pin_bruteforce_tiny, pin_chunked_loops, pin_full_causal, pin_block_diagonal, pin_first_token, pin_constant_v,
     pin_zero_query, pin_invariants, pin_pages_worked_example, pin_pages_sparsity_table,
-    pin_granularity, pin_closed_form_pairs, pin_lse_merge, pin_pooling_linearity,
+    pin_granularity, pin_closed_form_pairs, pin_query_lists_hand_example, pin_query_lists_transpose,
+    pin_lse_merge, pin_pooling_linearity,
     pin_gate_rounding, pin_row_mode_matches, pin_decode_full_attention, pin_decode_own_block,
     pin_decode_first_token, pin_decode_brute_selection, pin_decode_matches_prefill_row,
     pin_backward_full_causal, pin_backward_block_diagonal, pin_backward_brute, pin_backward_finite_difference,

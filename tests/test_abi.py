@@ -189,6 +189,28 @@ def test_backward_argument_checks(lib):
         assert backward(lib, ptrs=tuple(ptrs)) == UNSUPPORTED, i
 
 
+def test_query_lists_argument_checks(lib):
+    """moba_block_query_lists: the same shape checks as the gate, plus the
+    qidx capacity (the number of (query, past block) pairs, a closed form)."""
+    def lists(N=1024, H=2, D=128, B=128, topk=3, ptrs=(A, A, A, A, A), qidx_len=None):
+        n = N // B if B > 0 and N % B == 0 else 0
+        pairs = H * sum(B * min(topk - 1, j) for j in range(n))
+        return lib.moba_block_query_lists(*ptrs, pairs if qidx_len is None else qidx_len, N, H, D, B, topk, None)
+    for i in range(5):
+        ptrs = [A] * 5
+        ptrs[i] = None
+        assert lists(ptrs=tuple(ptrs)) == INVALID
+        ptrs[i] = A + 4
+        assert lists(ptrs=tuple(ptrs)) == UNSUPPORTED
+    for kw in (dict(N=0), dict(H=0), dict(topk=0), dict(B=0), dict(N=1000, B=128)):
+        assert lists(**kw) == INVALID, kw
+    for kw in (dict(D=96), dict(N=960, B=96), dict(N=64 * 100, B=64, topk=33)):
+        assert lists(**kw) == UNSUPPORTED, kw
+    # 1024 tokens, 8 blocks of 128, top-3: 2 * 128 * (0 + 1 + 2 * 6) = 3328 pairs.
+    assert lists(qidx_len=3327) == INVALID
+    assert lists(topk=1, qidx_len=-1) == INVALID
+
+
 def test_topk_for_sparsity_matches_oracle(lib):
     """Host-only helper (no GPU work): the library's dynamic k equals the oracle's."""
     from oracle import topk_for_sparsity

@@ -132,6 +132,93 @@ def test_workload(moba, name):
     run_case(moba, q, k, v, w.block_size, w.topk, w.dtype, rows=rows, full_out=(count is None))
 
 
+# (N, H, D, B, topk, seed): several gate tiles, a ragged last tile
+# (N % 128 = 64) with B = 64 (a tile spans two blocks), topk = 1 (every list
+# empty), topk > n (every past block listed) and the largest ranked topk.
+LISTS = [
+    (2048, 2, 128, 256, 3, 31),
+    (2368, 3, 64, 64, 5, 32),
+    (1024, 2, 128, 128, 1, 33),
+    (1024, 1, 64, 64, 40, 34),
+    (8192, 1, 128, 128, 32, 35),
+]
+
+
+def _lists_from_selection(sel, B):
+    """The lists a selection defines, by a stable sort of (head, block, query)
+    keys over its (query, past block) pairs (test code, independent of the
+    oracle's loops)."""
+    H, N, _ = sel.shape
+    n = N // B
+    t = np.broadcast_to(np.arange(N, dtype=np.int64)[None, :, None], sel.shape)
+    h = np.broadcast_to(np.arange(H, dtype=np.int64)[:, None, None], sel.shape)
+    keep = (sel >= 0) & (sel < t // B)
+    e = h[keep] * n + sel[keep]
+    tk = t[keep]
+    order = np.lexsort((tk, e))
+    offs = np.concatenate([[0], np.cumsum(np.bincount(e, minlength=H * n))])
+    return offs, tk[order]
+
+
+def _check_lists(moba, qd, kd, B, topk):
+    """Runs moba_block_query_lists; checks its selection against the gate entry
+    point and its lists against the selection (every pair once, ascending,
+    closed-form total). Returns the selection and lists on the host."""
+    H, N = qd.shape[1], qd.shape[0]
+    log(f"  gpu: block_query_lists N={N} H={H} B={B} topk={topk}")
+    sel, offs, qidx = moba.block_query_lists(qd, kd, B, topk)
+    sel_gate = moba.gate_topk(qd, kd, B, topk)
+    torch.cuda.synchronize()
+    gsel, goffs, gq = sel.cpu().numpy(), offs.cpu().numpy().astype(np.int64), qidx.cpu().numpy()
+    assert np.array_equal(gsel, sel_gate.cpu().numpy())
+    n = N // B
+    assert goffs[-1] == H * sum(B * min(topk - 1, j) for j in range(n)) == gq.shape[0]
+    toffs, tq = _lists_from_selection(gsel, B)
+    assert np.array_equal(goffs, toffs)
+    assert np.array_equal(gq, tq)
+    return gsel, goffs, gq
+
+
+@pytest.mark.parametrize("case", LISTS, ids=lambda c: "N{}_H{}_D{}_B{}_k{}".format(*c[:5]))
+def test_query_lists(moba, case):
+    """The regrouped query lists (the queries of every past block, ascending)
+    against the oracle's regrouping of the oracle's selection; rows where the
+    two selections differ (near-ties only) are left out of both."""
+    from oracle import query_lists, select_blocks
+    N, H, D, B, topk, seed = case
+    log(f"case lists {case}")
+    q, k, _ = synth.make_qkv(N, H, D, seed=[seed, 0], dtype="bf16")
+    qd, kd = to_device(q, "bf16"), to_device(k, "bf16")
+    gsel, goffs, gq = _check_lists(moba, qd, kd, B, topk)
+    ref_sel, _ = select_blocks(q, k, B, topk)
+    cmp = compare_selection(gsel, ref_sel, q, k, B, topk)
+    assert not cmp["bad"], cmp["bad"][:5]
+    ref_offs, ref_q = query_lists(ref_sel, B)
+    differ = np.any(gsel != ref_sel, axis=2)            # [H, N]
+    n = N // B
+    for e in range(H * n):
+        got = gq[goffs[e]:goffs[e + 1]]
+        want = ref_q[ref_offs[e]:ref_offs[e + 1]]
+        hd = differ[e // n]
+        assert np.array_equal(got[~hd[got]], want[~hd[want]]), e
+    log(f"  lists: {goffs[-1]} pairs, {int(differ.sum())} near-tie rows left out")
+
+
+def test_query_lists_h32(moba):
+    """Query lists of the h32 workload (32 heads, 32768 tokens, 64 blocks of
+    512, top-3): the transpose of the selection, with the selection checked
+    against the oracle on sampled rows."""
+    from oracle import select_blocks
+    w, q, k, _ = synth.make_workload("h32")
+    qd, kd = to_device(q, "bf16"), to_device(k, "bf16")
+    gsel, goffs, _ = _check_lists(moba, qd, kd, w.block_size, w.topk)
+    rows = synth.sample_rows(w.N, 2048, synth.SAMPLE_SEED["h32"])
+    ref_sel, _ = select_blocks(q, k, w.block_size, w.topk, rows=rows)
+    cmp = compare_selection(gsel[:, rows], ref_sel, q, k, w.block_size, w.topk, rows=rows)
+    assert not cmp["bad"], cmp["bad"][:5]
+    log(f"  h32 lists: {goffs[-1]} pairs, sampled sel mismatch {cmp['mismatch']} (exempt {cmp['exempt']})")
+
+
 def test_needles_are_found(moba):
     """The planted needle blocks of the 128K workload are chosen far more often
     than an average past block."""

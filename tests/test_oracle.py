@@ -30,6 +30,12 @@ MUTATIONS = {
                                 "sorted(order[i, :topk].tolist())"),
     "gate_chunk_offset_dropped": ("sel[h, c0 + i, :len(row)] = row", "sel[h, i, :len(row)] = row"),
     "dense_chunk_drops_last_row": ("idx = in_j[c0:c0 + max_rows_chunk]", "idx = in_j[c0:c0 + max_rows_chunk - 1]"),
+    "lists_include_own_block": ("                if 0 <= b < j:\n                    lists[h][b].append(t)",
+                                "                if 0 <= b <= j:\n                    lists[h][b].append(t)"),
+    "lists_descending": ("for t in range(N):                      # ascending t: every list comes out ascending",
+                         "for t in range(N - 1, -1, -1):"),
+    "lists_block_major": ("    for h in range(H):\n        for b in range(n):\n            qidx.extend(lists[h][b])",
+                          "    for b in range(n):\n        for h in range(H):\n            qidx.extend(lists[h][b])"),
     "causal_mask_off_by_one": ("chosen[:, key_block] & (key_pos[None, :] <= t[:, None])",
                                "chosen[:, key_block] & (key_pos[None, :] < t[:, None] + 2)"),
     "future_blocks_compete": ("neg[np.arange(n)[None, :] >= jj[:, None]] = np.inf",
