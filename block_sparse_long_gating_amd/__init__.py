@@ -18,7 +18,9 @@ __all__ = ["prefill", "gate_topk", "block_mean_keys", "block_query_lists", "Moba
            "StageEvents", "STAGES", "STATUS", "MAX_TOPK", "MAX_BLOCKS", "debug_poison_workspace"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libmoba.so")
+# MOBA_LIBRARY selects another build of the library (the host-sanitized debug
+# build); by default the in-tree libmoba.so is loaded.
+_LIB_PATH = os.environ.get("MOBA_LIBRARY") or os.path.join(_HERE, "libmoba.so")
 _lib = None
 
 STATUS = {0: "MOBA_OK", 1: "MOBA_ERR_INVALID_ARG", 2: "MOBA_ERR_UNSUPPORTED", 3: "MOBA_ERR_HIP",

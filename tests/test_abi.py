@@ -251,3 +251,27 @@ def test_varlen_argument_checks(lib):
     assert g(None, A, A, A, A, ok, 2, 2, 128, 128, 3, None) == INVALID
     assert lib.moba_gate_topk_varlen(A, A, A, cu(0, 300), 1, 2, 128, 128, 3, None) == INVALID
     assert lib.moba_prefill_bwd_varlen(A, A, A, A, A, A, A, A, A, ok, 2, 2, 96, 128, 3, None) == UNSUPPORTED
+
+
+def test_no_device_is_a_hip_error(lib):
+    """Without a GPU, calls whose arguments pass the checks stop at the device
+    lookup with MOBA_ERR_HIP and the HIP error kept for moba_last_hip_error
+    (on a machine with a GPU these fake pointers must never reach a kernel, so
+    the test only runs where there is none)."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: the fake pointers would be launched on")
+    HIP_ERROR_NO_DEVICE = 100
+    calls = [
+        lambda: prefill(lib),
+        lambda: prefill(lib, f32=True),
+        lambda: gate(lib),
+        lambda: pool(lib),
+        lambda: decode(lib),
+        lambda: backward(lib),
+        lambda: lib.moba_block_query_lists(A, A, A, A, A, 3328, 1024, 2, 128, 128, 3, None),
+        lambda: lib.moba_decode_fwd_noalloc(A, A, A, None, 0, A, A, None, 1000, 2, 128, 128, 3, None),
+    ]
+    for i, call in enumerate(calls):
+        assert call() == 3, i
+        assert lib.moba_last_hip_error() == HIP_ERROR_NO_DEVICE, i
