@@ -244,13 +244,17 @@ __global__ __launch_bounds__(256) void gate_mfma_kernel(const bf16* __restrict__
         const int brow = min(bc * 32 + qn, n - 1);
 #pragma unroll
         for (int pc = 0; pc < 3; ++pc) {
+          // All operands of one piece are read before its products, so the
+          // reads overlap one another instead of each product waiting for its own.
+          bf16x8 av[D / 16];
 #pragma unroll
-          for (int c = 0; c < D / 16; ++c) {
-            const bf16x8 av = kLds ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
-                                         plds + brow * kRow + pc * D * 2 + 32 * c + 16 * half))
-                                   : load_bf16x8(hp + static_cast<int64_t>(brow) * 3 * D + pc * D + 16 * c + 8 * half);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qop[c], acc, 0, 0, 0);
-          }
+          for (int c = 0; c < D / 16; ++c)
+            av[c] = kLds ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                               plds + brow * kRow + pc * D * 2 + 32 * c + 16 * half))
+                         : load_bf16x8(hp + static_cast<int64_t>(brow) * 3 * D + pc * D + 16 * c + 8 * half);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int c = 0; c < D / 16; ++c) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[c], qop[c], acc, 0, 0, 0);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
