@@ -237,6 +237,7 @@ __device__ __forceinline__ void store4(void* addr, float data) {
 // items with the merge fused in: two per past selection of the block's queries).
 struct Desc {
   int h, b, start, count, nkt, np;
+  int64_t kv_row;   // the block's first key / value row of head h, in rows of D elements
 };
 
 template <bool kCausal, bool kFused>
@@ -284,6 +285,7 @@ __device__ __forceinline__ Desc item_desc(const AttnArgs<bf16>& a, int64_t idx) 
   d.count = static_cast<int>(uniform_u32(d.count));
   d.nkt = static_cast<int>(uniform_u32(d.nkt));
   d.np = static_cast<int>(uniform_u32(d.np));
+  d.kv_row = static_cast<int64_t>(d.b) * a.B * a.H + d.h;
   return d;
 }
 
@@ -541,6 +543,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
   const int half = lane >> 5;
   const float c2 = a.scale_log2;
   const int64_t row_el = static_cast<int64_t>(a.H) * D;        // elements between consecutive tokens
+  const int64_t tile_el = kKTile * row_el;                      // elements between consecutive K/V tiles
   const uint32_t row_bytes = static_cast<uint32_t>(row_el * 2);
   const bool hi_rounds = w < L::kWindows % kWaves || L::kWindows % kWaves == 0;
 
@@ -649,8 +652,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs<bf16> a
         }
       }
     } else if (j >= 2) {
-      const int64_t r0 = static_cast<int64_t>(d.b) * a.B + kKTile * (j - 2);
-      const uint64_t kb = uniform_ptr(a.k + (r0 * a.H + d.h) * D), vb = uniform_ptr(a.v + (r0 * a.H + d.h) * D);
+      // Rows b * B + kKTile * (j - 2) onwards: the item's offset plus j - 2 tile strides.
+      const int64_t off = d.kv_row * D + static_cast<int64_t>(j - 2) * tile_el;
+      const uint64_t kb = uniform_ptr(a.k + off), vb = uniform_ptr(a.v + off);
 #pragma unroll
       for (int u = 0; u < L::kRoundsHi; ++u)
         if (u >= u0 && u < u1 && (u < L::kRoundsLo || hi_rounds))
