@@ -72,6 +72,39 @@ def past_pairs(N: int, B: int, topk: int) -> int:
     return sum(B * B * min(topk - 1, j) for j in range(n))
 
 
+def stage_rooflines(w, stage_ms: dict) -> dict:
+    """Per-stage bounds of the prefill from the stage times: bytes each stage
+    must move in this design over its time, against the HBM peak (the pool,
+    the gate and the own-block pass with the merge fused in are bound by HBM;
+    the past-block pass is the MFMA-bound kernel of `roofline`)."""
+    N, H, D, B, k = w.N, w.H, w.D, w.block_size, w.topk
+    n = N // B
+    lmax = min(k - 1, n - 1)
+    list_entries = H * sum(B * min(k - 1, j) for j in range(n))
+    tensor = N * H * D * 2                     # one bf16 [N][H][D] tensor
+    parts = {
+        # K read once; fp32 means and their 3-way bf16 split written.
+        "pool": ("pool", tensor + H * n * D * (4 + 6),
+                 "K read once; K-bar fp32 and its bf16 split written"),
+        # Q read once; the selection rows, in-tile ranks and per-tile counts written.
+        "gate": ("gate", tensor + H * N * (k + lmax) * 4 + H * n * -(-N // 128) * 4,
+                 "Q read once; selection rows, in-tile ranks and per-tile counts written"),
+        # Own block: Q, K, V read once; past partial rows (bf16) and their lse read
+        # back; out and lse written.
+        "attn_own_merge": ("attn_own", 3 * tensor + list_entries * (2 * D + 4) + tensor + H * N * 4,
+                           "Q, K, V read once; past partials (bf16 rows + lse) read back; out and lse written"),
+    }
+    out = {}
+    for name, (stage, nbytes, what) in parts.items():
+        t = stage_ms.get(stage, 0.0) + (stage_ms.get("merge", 0.0) if name == "attn_own_merge" else 0.0)
+        gbs = nbytes / (t * 1e-3) / 1e9 if t > 0 else 0.0
+        out[name] = {"bound": "hbm", "bytes": nbytes, "us": 1e3 * t, "achieved": gbs, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "bytes_counted": what}
+    out["timing"] = ("stage times from HIP events the library records at its stage boundaries "
+                     "(launch gaps included)")
+    return out
+
+
 def row_pairs(rows: np.ndarray, B: int, topk: int) -> int:
     j = rows // B
     return int(np.sum(np.minimum(topk - 1, j) * B + rows % B + 1))
@@ -606,6 +639,7 @@ def main():
             "launch_timing": f"{args.steps} further calls with HIP events around this launch "
                              f"({ms_with_events:.3f} ms per call with the events)",
         },
+        "stage_rooflines": stage_rooflines(w, stage_ms),
         "device": info,
     }
 
