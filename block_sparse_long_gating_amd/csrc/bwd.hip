@@ -68,16 +68,19 @@ struct BwdLay {
 
 // MFMA over D: rows from a row-major LDS tile (A operand, per-lane pointer to
 // row l % 32 at byte 16 (l / 32)), columns from registers (B operand).
+// All D / 16 row pieces are read before the products, so the reads overlap one
+// another instead of each product waiting for its own.
 template <int D>
 __device__ __forceinline__ f32x16 rows_by_regs(const char* ap, const bf16x8 (&b)[D / 16]) {
   f32x16 s;
 #pragma unroll
   for (int r = 0; r < 16; ++r) s[r] = 0.f;
+  bf16x8 av[D / 16];
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-    const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ap + 32 * c));
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[c], s, 0, 0, 0);
-  }
+  for (int c = 0; c < D / 16; ++c) av[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ap + 32 * c));
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[c], b[c], s, 0, 0, 0);
   return s;
 }
 
