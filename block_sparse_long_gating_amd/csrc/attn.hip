@@ -418,7 +418,17 @@ __device__ __forceinline__ void tile_pair(const char* kp, const char* vp, const 
                                           int half, float c2, F&& issue) {
   using L = Lay<D>;
   constexpr int kQC = D / 16;
-  f32x16 s0 = scores<D>(kp, q);
+  // The first half's K operands all requested before its products (the step
+  // opens with them, right after the barrier).
+  bf16x8 ka[kQC];
+#pragma unroll
+  for (int c = 0; c < kQC; ++c) ka[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kp + 32 * c));
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 s0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s0[r] = 0.f;
+#pragma unroll
+  for (int c = 0; c < kQC; ++c) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], q[c], s0, 0, 0, 0);
   __builtin_amdgcn_sched_barrier(0);
   issue(0);
   __builtin_amdgcn_sched_barrier(0);
