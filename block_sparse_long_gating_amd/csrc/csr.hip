@@ -153,16 +153,21 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   const int64_t t1 = min(N, t0 + kQTile);
   const int jmax = static_cast<int>((t1 - 1) / B);   // the tile's past blocks are all below its last block
   if (jmax == 0) return;
-  // Per-block share of the tile (its count), then the exclusive prefix over blocks.
+  // Per-block share of the tile (its count), then the exclusive prefix over
+  // blocks; and the list position of the tile's first entry in each list.
+  const int jpad = (jmax + 3) & ~3;
   int32_t* const pre = csm;                                              // [jmax]
-  int2* const ent = reinterpret_cast<int2*>(csm + ((jmax + 3) & ~3));    // [kQTile * lmax]: (position, query)
+  int32_t* const first = csm + jpad;                                     // [jmax]
+  int2* const ent = reinterpret_cast<int2*>(csm + 2 * jpad);             // [kQTile * lmax]: (position, query)
   const int per = (jmax + 255) / 256;
   const int b0 = min(jmax, tid * per), b1 = min(jmax, b0 + per);
   int64_t sum = 0;
   for (int b = b0; b < b1; ++b) {
     const int64_t e = hn + b;
-    const int c = (tile + 1 < ntiles ? cnt[e * ntiles + tile + 1] : totals[e]) - cnt[e * ntiles + tile];
+    const int before = cnt[e * ntiles + tile];
+    const int c = (tile + 1 < ntiles ? cnt[e * ntiles + tile + 1] : totals[e]) - before;
     pre[b] = c;
+    first[b] = offs[e] + before;
     sum += c;
   }
   int64_t total;
@@ -184,8 +189,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
     const int64_t g = static_cast<int64_t>(h) * N + t;
     const int b = sel[g * topk + s];
     const int r = rk[g * lmax + s];
-    const int64_t e = hn + b;
-    const int32_t pos = offs[e] + cnt[e * ntiles + tile] + r;
+    const int32_t pos = first[b] + r;
     inv[g * lmax + s] = pos;
     ent[pre[b] + r] = make_int2(pos, static_cast<int32_t>(t));
   }
@@ -203,8 +207,9 @@ hipError_t launch_csr(const Problem& p, const Workspace& ws, const int32_t* sel,
   const int64_t E = static_cast<int64_t>(p.H) * p.n;
   scan_tiles_kernel<<<static_cast<unsigned>(E), 256, 0, stream>>>(ws.cnt, ws.totals, p.ntiles);
   build_lists_kernel<<<1, kListThreads, 0, stream>>>(ws.totals, ws.offs, ws.istart, ws.counters, E);
-  // LDS: the per-block prefix of a tile's past blocks (at most n) and its (position, query) pairs.
-  const size_t smem = static_cast<size_t>((p.n + 3) & ~3) * 4 + static_cast<size_t>(kQTile) * p.lmax * 8;
+  // LDS: the per-block prefix and first list positions of a tile's past blocks
+  // (at most n each) and its (position, query) pairs.
+  const size_t smem = static_cast<size_t>((p.n + 3) & ~3) * 8 + static_cast<size_t>(kQTile) * p.lmax * 8;
   dim3 grid(static_cast<unsigned>(p.ntiles), static_cast<unsigned>(p.H));
   scatter_kernel<<<grid, 256, smem, stream>>>(sel, ws.rk, ws.cnt, ws.totals, ws.offs, ws.istart, ws.qidx, ws.inv,
                                               ws.items, p.N, p.H, p.B, p.n, p.topk, p.lmax, p.ntiles, p.blo);
