@@ -215,6 +215,14 @@ moba::Workspace bind(const WsPlan& w, char* base, bool full) {
 }
 
 int alloc_ws(DeviceState* st, size_t bytes, hipStream_t stream, char** out) {
+  // A stream under capture would record the pool allocation and its free as
+  // graph memory nodes, which the allocating calls do not support: they
+  // refuse capture before anything is enqueued. (The allocation-free decode
+  // step takes its workspace from a fixed device array instead.)
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  const hipError_t ce = hipStreamIsCapturing(stream, &capture);
+  if (ce != hipSuccess) return hip_fail(ce);
+  if (capture != hipStreamCaptureStatusNone) return MOBA_ERR_UNSUPPORTED;
   std::call_once(st->pool_once, init_pool, st);
   if (st->pool_error != hipSuccess) return hip_fail(st->pool_error);
   void* p = nullptr;

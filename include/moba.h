@@ -46,7 +46,10 @@
  *   MOBA_ERR_UNSUPPORTED   D not 64 or 128, block_size not a multiple of 64,
  *                          a pointer not 16-byte aligned, more than
  *                          MOBA_MAX_BLOCKS blocks, topk in (MOBA_MAX_TOPK, n),
- *                          N >= 2^28, or a device that is not gfx950.
+ *                          N >= 2^28, or a device that is not gfx950; also a
+ *                          call that takes pool workspace on a stream under
+ *                          graph capture (nothing is enqueued: the pool
+ *                          allocation is not recorded into graphs).
  *   MOBA_ERR_HIP           a HIP runtime call or launch failed; the HIP error
  *                          code is kept per thread (moba_last_hip_error).
  *   MOBA_ERR_OUT_OF_MEMORY the workspace could not be allocated.
@@ -298,7 +301,9 @@ int moba_decode_fwd(const void* q, const void* k, const void* v, const float* kb
  * one GPU share the array and it keeps the last call's contents (every byte a
  * call reads it has written first): calls that may overlap on one GPU (other
  * streams, or other threads without ordering) race and must be serialised by
- * the caller; calls ordered on one stream are safe.
+ * the caller; calls ordered on one stream are safe. Under capture it records
+ * kernel nodes only (no memory nodes); replaying such a graph is not exercised
+ * by this library's tests.
  */
 #define MOBA_NOALLOC_SCRATCH_BYTES (64u << 20)
 int moba_decode_fwd_noalloc(const void* q, const void* k, const void* v, const float* kbar, int32_t kbar_blocks,
