@@ -133,26 +133,46 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   const int tid = static_cast<int>(threadIdx.x);
   const int64_t hn = static_cast<int64_t>(h) * n;
 
-  // Work items of this workgroup's lists.
-  for (int b = tile; b < n; b += ntiles) {
-    const int64_t e = hn + b;
-    const int len = totals[e];
-    const int i0 = istart[e], p0 = offs[e];
-    for (int c = tid; c * kAttnTile < len; c += 256) {
-      WorkItem wi;
-      wi.h = h;
-      wi.b = b;
-      wi.start = p0 + c * kAttnTile;
-      wi.count = min(kAttnTile, len - c * kAttnTile);
-      items[i0 + c] = wi;
+  // Work items of this workgroup's lists (written last: nothing below waits on them).
+  auto write_items = [&]() {
+    for (int b = tile; b < n; b += ntiles) {
+      const int64_t e = hn + b;
+      const int len = totals[e];
+      const int i0 = istart[e], p0 = offs[e];
+      for (int c = tid; c * kAttnTile < len; c += 256) {
+        WorkItem wi;
+        wi.h = h;
+        wi.b = b;
+        wi.start = p0 + c * kAttnTile;
+        wi.count = min(kAttnTile, len - c * kAttnTile);
+        items[i0 + c] = wi;
+      }
     }
-  }
-  if (lmax == 0) return;
-
+  };
   const int64_t t0 = static_cast<int64_t>(tile) * kQTile;
   const int64_t t1 = min(N, t0 + kQTile);
   const int jmax = static_cast<int>((t1 - 1) / B);   // the tile's past blocks are all below its last block
-  if (jmax == 0) return;
+  if (lmax == 0 || jmax == 0) {
+    write_items();
+    return;
+  }
+  // (query, kept past block) pair i of the tile: query t0 + i / lmax, slot i % lmax.
+  const int nq = static_cast<int>(t1 - t0);
+  auto load_pair = [&](int i, int& b, int& r, int64_t& t) -> bool {
+    const int qi = i / lmax, s = i - qi * lmax;
+    t = t0 + qi;
+    const int j = static_cast<int>(t / B);
+    if (s >= kept_past(j, blo != nullptr ? blo[j] : 0, topk)) return false;
+    const int64_t g = static_cast<int64_t>(h) * N + t;
+    b = sel[g * topk + s];
+    r = rk[g * lmax + s];
+    return true;
+  };
+  // The thread's first pair is read before the list positions (it does not
+  // depend on them), so the two reads overlap.
+  int b_first = 0, r_first = 0;
+  int64_t t_first = 0;
+  const bool has_first = tid < nq * lmax && load_pair(tid, b_first, r_first, t_first);
   // Per-block share of the tile (its count), then the exclusive prefix over
   // blocks; and the list position of the tile's first entry in each list.
   const int jpad = (jmax + 3) & ~3;
@@ -180,15 +200,19 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   if (tid == 0) s_total = static_cast<int32_t>(total);
   __syncthreads();
   // Pairs in query order: coalesced reads of sel and rk and writes of inv.
-  const int nq = static_cast<int>(t1 - t0);
   for (int i = tid; i < nq * lmax; i += 256) {
+    int b, r;
+    int64_t t;
+    if (i == tid) {
+      if (!has_first) continue;
+      b = b_first;
+      r = r_first;
+      t = t_first;
+    } else if (!load_pair(i, b, r, t)) {
+      continue;
+    }
     const int qi = i / lmax, s = i - qi * lmax;
-    const int64_t t = t0 + qi;
-    const int j = static_cast<int>(t / B);
-    if (s >= kept_past(j, blo != nullptr ? blo[j] : 0, topk)) continue;
-    const int64_t g = static_cast<int64_t>(h) * N + t;
-    const int b = sel[g * topk + s];
-    const int r = rk[g * lmax + s];
+    const int64_t g = static_cast<int64_t>(h) * N + t0 + qi;
     const int32_t pos = first[b] + r;
     inv[g * lmax + s] = pos;
     ent[pre[b] + r] = make_int2(pos, static_cast<int32_t>(t));
@@ -199,6 +223,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
     const int2 x = ent[k];
     qidx[x.x] = x.y;
   }
+  write_items();
 }
 
 }  // namespace
