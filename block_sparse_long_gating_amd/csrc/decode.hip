@@ -138,6 +138,13 @@ __global__ __launch_bounds__(256) void decode_gate_kernel(DecodeArgs a) {
   }
 }
 
+typedef unsigned u32x4nt __attribute__((ext_vector_type(4)));
+
+// 16-byte non-temporal load (data read once).
+__device__ __forceinline__ bf16x8 load_stream(const bf16* p) {
+  return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4nt*>(p)));
+}
+
 // Partial attention of one (head, kept block, chunk) unit; the last unit of a
 // head to finish also combines the head.
 template <int D>
@@ -170,12 +177,15 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
   for (int64_t kk = k0 + g; kk < k1; kk += kDecKeys * kGroups) {
     // kDecKeys keys per lane group, kGroups apart (a key past the end re-reads
     // kk and is masked out).
+    // This path serves the long attended sets (every block kept, or more keys
+    // than the one-launch step takes), whose keys and values stream through
+    // once: non-temporal loads (h32, every block kept: 113.6 -> 100.0 us).
     bf16x8 k8[kDecKeys], v8[kDecKeys];
 #pragma unroll
     for (int x = 0; x < kDecKeys; ++x) {
       const int64_t kx = kk + x * kGroups < k1 ? kk + x * kGroups : kk;
-      k8[x] = load_bf16x8(a.k + kx * row_el + col);
-      v8[x] = load_bf16x8(a.v + kx * row_el + col);
+      k8[x] = load_stream(a.k + kx * row_el + col);
+      v8[x] = load_stream(a.v + kx * row_el + col);
     }
     float s[kDecKeys];
 #pragma unroll
